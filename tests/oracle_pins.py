@@ -1,0 +1,391 @@
+"""Pins for the fp64 oracle: checks against facts fixed by mathematics, not by the oracle.
+
+Each ``pin_*`` raises AssertionError on failure.  ``tests/test_oracle_pins.py`` runs them
+against the oracle as it is, and again against planted mistakes (a dropped term, a
+wrong sign, a transposed operand, a wrong head map, an off-by-one in the fold rule) to
+show that each plausible mistake fails at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+from fractions import Fraction
+from types import SimpleNamespace
+
+import numpy as np
+
+import oracle.delta_rule as dr
+import oracle.replay as rp
+from oracle import exact
+
+# ----------------------------------------------------------------------------- helpers
+
+
+def _frac_vec(rng, n, denom=8):
+    return [Fraction(int(x), denom) for x in rng.integers(-denom, denom + 1, size=n)]
+
+
+def _tiny_tokens(rng, T, dk, dv, kda):
+    toks = []
+    for _ in range(T):
+        q = _frac_vec(rng, dk)
+        k = _frac_vec(rng, dk)
+        v = _frac_vec(rng, dv)
+        beta = Fraction(int(rng.integers(1, 5)), 4)
+        if kda:
+            alpha = [Fraction(int(rng.integers(4, 8)), 8) for _ in range(dk)]
+        else:
+            alpha = Fraction(int(rng.integers(4, 8)), 8)
+        toks.append((q, k, v, beta, alpha))
+    return toks
+
+
+def _f(x):
+    return np.array([float(e) for e in x]) if isinstance(x, list) else float(x)
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, float), np.asarray(b, float)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def _inputs(B, T, hk, hv, dk, dv, kda, rng, beta=None, alpha=None, unit=True):
+    def unit_vec(shape):
+        x = rng.standard_normal(shape)
+        return x / np.linalg.norm(x, axis=-1, keepdims=True) if unit else x
+    q = unit_vec((B, T, hk, dk))
+    k = unit_vec((B, T, hk, dk))
+    v = rng.standard_normal((B, T, hv, dv))
+    b = rng.uniform(0, 1, (B, T, hv)) if beta is None else np.full((B, T, hv), beta)
+    gshape = (B, T, hv, dk) if kda else (B, T, hv)
+    g = rng.uniform(0.3, 0.99, gshape) if alpha is None else np.full(gshape, alpha)
+    return SimpleNamespace(q=q, k=k, v=v, beta=b, gate=g)
+
+
+def _layer(S0, L, hk, hv, dk, dv, kda, cursor=None, rng=None):
+    nslots = S0.shape[0]
+    rk = np.full((nslots, L, hk, dk), np.nan)
+    rd = np.full((nslots, L, hv, dv), np.nan)
+    rg = np.full((nslots, L, hv, dk) if kda else (nslots, L, hv), np.nan)
+    if cursor is not None:
+        for s in range(nslots):
+            c = int(cursor[s])
+            rk[s, :c] = rng.standard_normal((c, hk, dk)) / np.sqrt(dk)
+            rd[s, :c] = rng.standard_normal((c, hv, dv))
+            rg[s, :c] = rng.uniform(0.3, 0.99, rg[s, :c].shape)
+    return rp.ReplayLayer(S0, rk, rd, rg, kda, hv // hk, L)
+
+
+def run_both(S0, steps_inputs, accepts, slots, L, T, hk, hv, kda, policies,
+             cursor0=None, ring_rng=None, force_masks=None):
+    """Run the replay state machine and the token-stream definition side by side.
+    Returns (max relative output gap, max relative committed-state gap, fused folds,
+    cursor trace)."""
+    nslots = S0.shape[0]
+    dk, dv = S0.shape[2], S0.shape[3]
+    cursor = np.zeros(nslots, np.int32) if cursor0 is None else cursor0.copy()
+    fold_len = np.zeros(nslots, np.int32)
+    layer = _layer(S0, L, hk, hv, dk, dv, kda, cursor if cursor0 is not None else None,
+                   ring_rng)
+    ts = rp.TokenStream.from_replay(layer, cursor)
+    gap_o = gap_s = 0.0
+    trace = []
+    for j, (inp, acc) in enumerate(zip(steps_inputs, accepts)):
+        o_rep, wp = rp.verify(layer, cursor, slots, inp)
+        o_def, _ = ts.verify(slots, inp)
+        live = slots >= 0
+        gap_o = max(gap_o, _rel(o_rep[live], o_def[live]))
+        pol, next_T = policies[j]
+        fm = None if force_masks is None else force_masks[j]
+        rp.cursor_advance(cursor, fold_len, slots, acc, T, L, pol, next_T, fm)
+        rp.commit_fold(layer, fold_len, slots)
+        ts.accept(slots, acc)
+        trace.append(cursor.copy())
+        for r, s in enumerate(slots):
+            if s < 0:
+                continue
+            assert 0 <= cursor[s] <= L
+            gap_s = max(gap_s, _rel(layer.committed_state(s, int(cursor[s])), ts.H[s]))
+    return gap_o, gap_s, layer.fused_folds, trace
+
+
+# ----------------------------------------------------------------------------- pins
+
+
+def pin_exact_rational():
+    """fp64 oracle vs exact rational dense literal form, GDN and KDA, several tokens."""
+    rng = np.random.default_rng(11)
+    for kda in (False, True):
+        dk, dv, T = 3, 2, 5
+        S0 = [_frac_vec(rng, dk) for _ in range(dv)]          # [dv][dk], key-to-value
+        toks = _tiny_tokens(rng, T, dk, dv, kda)
+        S_ex, outs_ex = exact.run(S0, toks, kda)
+        S = np.array([[float(x) for x in row] for row in S0]).T    # stored [dk, dv]
+        for t, (q, k, v, beta, alpha) in enumerate(toks):
+            S, _ = dr.token_update(S, _f(k), _f(v), _f(beta), _f(alpha), kda)
+            o = dr.readout(S, _f(q))
+            assert _rel(o, _f(outs_ex[t])) < 1e-13, ('output', kda, t)
+        S_ex_stored = np.array([[float(x) for x in row] for row in S_ex]).T
+        assert _rel(S, S_ex_stored) < 1e-13, ('state', kda)
+
+
+def pin_exact_grouped_heads():
+    """Grouped heads against the exact rule run per value head with key head h // G."""
+    rng = np.random.default_rng(12)
+    hk, G, dk, dv, T = 2, 2, 2, 3, 3
+    hv = hk * G
+    S0 = [[_frac_vec(rng, dk) for _ in range(dv)] for _ in range(hv)]
+    toks = [[_tiny_tokens(rng, 1, dk, dv, False)[0] for _ in range(hv)] for _ in range(T)]
+    # key-head inputs: token t, key head j takes q, k of value head j*G
+    q = np.array([[_f(toks[t][j * G][0]) for j in range(hk)] for t in range(T)])
+    k = np.array([[_f(toks[t][j * G][1]) for j in range(hk)] for t in range(T)])
+    v = np.array([[_f(toks[t][h][2]) for h in range(hv)] for t in range(T)])
+    beta = np.array([[_f(toks[t][h][3]) for h in range(hv)] for t in range(T)])
+    alpha = np.array([[_f(toks[t][h][4]) for h in range(hv)] for t in range(T)])
+    S = np.array([[[float(x) for x in row] for row in S0[h]] for h in range(hv)]).transpose(0, 2, 1)
+    for h in range(hv):
+        j = h // G
+        seq = [(toks[t][j * G][0], toks[t][j * G][1], toks[t][h][2], toks[t][h][3],
+                toks[t][h][4]) for t in range(T)]
+        _, outs = exact.run(S0[h], seq, False)
+        Sh = S.copy()
+        for t in range(T):
+            Sh, _ = dr.token_update(Sh, dr.expand_heads(k[t], G), v[t], beta[t], alpha[t], False)
+            o = dr.readout(Sh, dr.expand_heads(q[t], G))
+            assert _rel(o[h], _f(outs[t])) < 1e-13, ('grouped head', h, t)
+
+
+def pin_pure_decay():
+    """beta = 0: no writes, so o_t = (prod alpha) S0^T q_t (GDN) or S0^T (Gamma (.) q_t)
+    (KDA), through history replay, fused folds and commit folds."""
+    for kda in (False, True):
+        rng = np.random.default_rng(13)
+        hk, hv, dk, dv, L, T, steps = 1, 2, 4, 3, 5, 2, 7
+        S0 = rng.standard_normal((2, hv, dk, dv))
+        slots = np.array([1], np.int32)
+        layer = _layer(S0, L, hk, hv, dk, dv, kda)
+        cursor = np.zeros(2, np.int32)
+        fold_len = np.zeros(2, np.int32)
+        Gam = np.ones((hv, dk) if kda else (hv,))
+        for j in range(steps):
+            inp = _inputs(1, T, hk, hv, dk, dv, kda, rng, beta=0.0, alpha=None)
+            out, _ = rp.verify(layer, cursor, slots, inp)
+            a = np.array([int(rng.integers(1, T + 1))])
+            g = Gam.copy()
+            for t in range(T):
+                g = g * inp.gate[0, t]
+                qx = dr.expand_heads(inp.q[0, t], hv // hk)
+                want = np.einsum('hij,hi->hj', S0[1], g * qx) if kda else \
+                    g[:, None] * np.einsum('hij,hi->hj', S0[1], qx)
+                assert _rel(out[0, t], want) < 1e-12, ('pure decay', kda, j, t)
+            for t in range(int(a[0])):
+                Gam = Gam * inp.gate[0, t]
+            pol = rp.FOLD_FORCE if j == 5 else rp.FOLD_NONE
+            rp.cursor_advance(cursor, fold_len, slots, a, T, L, pol)
+            rp.commit_fold(layer, fold_len, slots)
+        assert layer.fused_folds >= 1
+
+
+def pin_identity_readout():
+    """alpha = 1, beta = 0, q = e_i  ->  o = row i of the stored state of each value head."""
+    rng = np.random.default_rng(14)
+    hk, hv, dk, dv = 2, 4, 5, 3
+    S0 = rng.standard_normal((hv, dk, dv))
+    for i in range(dk):
+        q = np.zeros((hk, dk))
+        q[:, i] = 1.0
+        k = rng.standard_normal((hk, dk))
+        S, _ = dr.token_update(S0, dr.expand_heads(k, 2), rng.standard_normal((hv, dv)),
+                               np.zeros(hv), np.ones(hv), False)
+        o = dr.readout(S, dr.expand_heads(q, 2))
+        assert np.array_equal(o, S0[:, i, :]), ('identity readout', i)
+
+
+def pin_write_then_read():
+    """beta = 1 and a unit key: afterwards S^T k = v whatever the old state and decay, so
+    q = k reads back v (GDN and KDA)."""
+    rng = np.random.default_rng(15)
+    for kda in (False, True):
+        hv, dk, dv = 3, 6, 4
+        S = rng.standard_normal((hv, dk, dv))
+        k = rng.standard_normal((hv, dk))
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        v = rng.standard_normal((hv, dv))
+        alpha = rng.uniform(0.2, 0.9, (hv, dk) if kda else (hv,))
+        S2, d = dr.token_update(S, k, v, np.ones(hv), alpha, kda)
+        assert _rel(dr.readout(S2, k), v) < 1e-13, ('write then read', kda)
+
+
+def pin_grouped_write():
+    """alpha = 1, beta = 1, k = e_i on key head j only: value heads h with h // G == j get
+    row i replaced by v exactly; every other head is unchanged."""
+    rng = np.random.default_rng(16)
+    hk, G, dk, dv = 3, 2, 4, 5
+    hv = hk * G
+    for j in range(hk):
+        for i in range(dk):
+            S0 = rng.standard_normal((hv, dk, dv))
+            k = np.zeros((hk, dk))
+            k[j, i] = 1.0
+            v = rng.standard_normal((hv, dv))
+            S, _ = dr.token_update(S0, dr.expand_heads(k, G), v, np.ones(hv), np.ones(hv), False)
+            for h in range(hv):
+                if h // G == j:
+                    assert np.allclose(S[h, i], v[h], rtol=0, atol=1e-14)
+                    others = [x for x in range(dk) if x != i]
+                    assert np.array_equal(S[h, others], S0[h, others])
+                else:
+                    assert np.array_equal(S[h], S0[h]), ('grouped write', j, h)
+
+
+def pin_replay_equals_sequential():
+    """Replay state machine == token-stream definition, every step, with history, fused
+    folds, commit folds, null rows and staggered cursors (fp64, 1e-12)."""
+    rng = np.random.default_rng(17)
+    for kda, T, L, pol in ((False, 1, 4, rp.FOLD_NONE), (False, 3, 8, rp.FOLD_LAZY),
+                           (True, 3, 7, rp.FOLD_NONE), (False, 4, 6, rp.FOLD_EVERY_COMMIT),
+                           (True, 2, 5, rp.FOLD_FORCE)):
+        hk, hv, dk, dv, B, steps = 2, 4, 6, 5, 4, 9
+        nslots = B + 2
+        S0 = rng.standard_normal((nslots, hv, dk, dv)) * 0.3
+        slots = np.array([3, -1, 0, 5], np.int32)
+        cursor0 = np.zeros(nslots, np.int32)
+        for s in (3, 0, 5):
+            cursor0[s] = int(rng.integers(0, L - T + 1))
+        ins = [_inputs(B, T, hk, hv, dk, dv, kda, rng) for _ in range(steps)]
+        accs = [rng.integers(0, T + 1, size=B).astype(np.int32) for _ in range(steps)]
+        fms = [rng.integers(0, 2, size=B).astype(np.uint8) for _ in range(steps)]
+        go, gs, nf, _ = run_both(S0, ins, accs, slots, L, T, hk, hv, kda,
+                                 [(pol, T)] * steps, cursor0, rng, fms)
+        assert go < 1e-12 and gs < 1e-12, ('replay vs sequential', kda, T, L, pol, go, gs)
+
+
+def pin_fold_invariance():
+    """Folding at any point changes nothing: a ring too large to ever fold, forced folds at
+    random steps, every-commit and lazy folds all give the same outputs (1e-12)."""
+    rng = np.random.default_rng(18)
+    for kda in (False, True):
+        hk, hv, dk, dv, B, T, steps = 1, 2, 4, 4, 3, 3, 10
+        S0 = rng.standard_normal((B, hv, dk, dv))
+        slots = np.arange(B, dtype=np.int32)
+        ins = [_inputs(B, T, hk, hv, dk, dv, kda, rng) for _ in range(steps)]
+        accs = [rng.integers(0, T + 1, size=B).astype(np.int32) for _ in range(steps)]
+        outs = []
+        for L, pols in ((T * steps, [(rp.FOLD_NONE, T)] * steps),
+                        (T * steps, [((rp.FOLD_FORCE if rng.random() < 0.4 else rp.FOLD_NONE), T)
+                                     for _ in range(steps)]),
+                        (T, [(rp.FOLD_EVERY_COMMIT, T)] * steps),
+                        (2 * T, [(rp.FOLD_LAZY, T)] * steps),
+                        (T + 1, [(rp.FOLD_NONE, T)] * steps)):
+            layer = _layer(S0, L, hk, hv, dk, dv, kda)
+            cursor = np.zeros(B, np.int32)
+            fl = np.zeros(B, np.int32)
+            o_all = []
+            for j in range(steps):
+                o, _ = rp.verify(layer, cursor, slots, ins[j])
+                o_all.append(o)
+                rp.cursor_advance(cursor, fl, slots, accs[j], T, L, *pols[j])
+                rp.commit_fold(layer, fl, slots)
+            outs.append((np.array(o_all), rp.materialize(layer, cursor, slots)))
+        for o, m in outs[1:]:
+            assert _rel(o, outs[0][0]) < 1e-12, ('fold invariance outputs', kda)
+            assert _rel(m, outs[0][1]) < 1e-12, ('fold invariance state', kda)
+
+
+def pin_cursor_bruteforce():
+    """Every accept sequence over 6 steps with T = 2, L = 4 (3^6 = 729), three policies:
+    cursor stays in [0, L], committed records sit at ring rows [0, cursor) in accept
+    order, and the replay outputs equal the definition's."""
+    T, L, steps = 2, 4, 6
+    hk = hv = 1
+    dk = dv = 2
+    rng = np.random.default_rng(19)
+    S0 = rng.standard_normal((1, hv, dk, dv))
+    ins = [_inputs(1, T, hk, hv, dk, dv, False, rng) for _ in range(steps)]
+    slots = np.array([0], np.int32)
+    for pol in (rp.FOLD_NONE, rp.FOLD_LAZY, rp.FOLD_EVERY_COMMIT):
+        for seq in itertools.product(range(T + 1), repeat=steps):
+            layer = _layer(S0, L, hk, hv, dk, dv, False)
+            ts = rp.TokenStream.from_replay(layer, np.zeros(1, np.int32))
+            cursor = np.zeros(1, np.int32)
+            fl = np.zeros(1, np.int32)
+            pending = []            # keys committed since the last fold, in order
+            for j, a in enumerate(seq):
+                n = int(cursor[0])
+                o, wp = rp.verify(layer, cursor, slots, ins[j])
+                o2, _ = ts.verify(slots, ins[j])
+                assert _rel(o, o2) < 1e-12
+                exp_base = 0 if n + T > L else n
+                assert wp[0] == exp_base
+                if exp_base == 0:
+                    pending = []
+                acc = np.array([a], np.int32)
+                folds_before = layer.fused_folds
+                rp.cursor_advance(cursor, fl, slots, acc, T, L, pol, T)
+                if pol == rp.FOLD_LAZY:
+                    # lazy: fold exactly when the next verify of width T would overflow
+                    assert (fl[0] > 0) == (exp_base + a + T > L)
+                    assert layer.fused_folds == 0
+                rp.commit_fold(layer, fl, slots)
+                ts.accept(slots, acc)
+                pending = pending + [ins[j].k[0, t] for t in range(a)]
+                if fl[0]:
+                    pending = []
+                assert 0 <= cursor[0] <= L and cursor[0] == len(pending)
+                for i, key in enumerate(pending):
+                    assert np.array_equal(layer.rk[0][i], key)
+            assert _rel(rp.materialize(layer, cursor, slots)[0], ts.H[0]) < 1e-12
+
+
+def pin_c0_fold_count():
+    """Tiny decode: capacity 4, one token per step, 12 steps -> the fused fold fires
+    exactly twice, at steps 4 and 8 (cursor after each step 1,2,3,4 | 1,2,3,4 | 1,2,3,4)."""
+    rng = np.random.default_rng(20)
+    L, T, steps = 4, 1, 12
+    S0 = rng.standard_normal((2, 1, 16, 16))
+    layer = _layer(S0, L, 1, 1, 16, 16, False)
+    cursor = np.zeros(2, np.int32)
+    fl = np.zeros(2, np.int32)
+    slots = np.array([1], np.int32)
+    fired = []
+    for j in range(steps):
+        before = layer.fused_folds
+        rp.verify(layer, cursor, slots, _inputs(1, T, 1, 1, 16, 16, False, rng))
+        if layer.fused_folds != before:
+            fired.append(j)
+        rp.cursor_advance(cursor, fl, slots, np.array([1], np.int32), T, L, rp.FOLD_NONE)
+    assert fired == [4, 8], fired
+    assert cursor[1] == 4
+
+
+def pin_nan_isolation():
+    """Non-finite v at rejected positions never reaches accepted outputs, committed
+    records or the folded state."""
+    rng = np.random.default_rng(21)
+    hk, hv, dk, dv, B, T, L, steps = 1, 2, 4, 4, 3, 4, 8, 6
+    S0 = rng.standard_normal((B, hv, dk, dv))
+    slots = np.arange(B, dtype=np.int32)
+    layer = _layer(S0, L, hk, hv, dk, dv, False)
+    cursor = np.zeros(B, np.int32)
+    fl = np.zeros(B, np.int32)
+    for j in range(steps):
+        inp = _inputs(B, T, hk, hv, dk, dv, False, rng)
+        acc = rng.integers(0, T, size=B).astype(np.int32)
+        for r in range(B):
+            for t in range(acc[r], T):
+                inp.v[r, t, int(rng.integers(hv)), int(rng.integers(dv))] = \
+                    (np.nan, np.inf, -np.inf)[int(rng.integers(3))]
+        with np.errstate(invalid='ignore'):
+            o, _ = rp.verify(layer, cursor, slots, inp)
+        for r in range(B):
+            assert np.all(np.isfinite(o[r, :acc[r]]))
+        pol = rp.FOLD_EVERY_COMMIT if j % 2 else rp.FOLD_LAZY
+        rp.cursor_advance(cursor, fl, slots, acc, T, L, pol, T)
+        rp.commit_fold(layer, fl, slots)
+        for s in range(B):
+            assert np.all(np.isfinite(layer.S[s]))
+            assert np.all(np.isfinite(layer.rd[s][:cursor[s]]))
+
+
+ALL_PINS = [pin_exact_rational, pin_exact_grouped_heads, pin_pure_decay, pin_identity_readout,
+            pin_write_then_read, pin_grouped_write, pin_replay_equals_sequential,
+            pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation]

@@ -1,0 +1,97 @@
+"""CPU tests: the fp64 oracle against its pins, and planted mistakes against the pins."""
+import numpy as np
+import pytest
+
+import oracle.delta_rule as dr
+import oracle.replay as rp
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    with np.errstate(invalid='ignore', over='ignore'):
+        pin()
+
+
+# ---------------------------------------------------------------- planted mistakes
+# Each mutant replaces one oracle function with a plausible wrong version.  The pins
+# must reject every one of them (at least one pin fails).
+
+def _tu_sign(S, k, v, beta, alpha, kda):
+    Sd = dr.decay(S, alpha, kda)
+    d = np.asarray(beta)[..., None] * (v + np.einsum('...ij,...i->...j', Sd, k))
+    return Sd + np.einsum('...i,...j->...ij', k, d), d
+
+
+def _tu_nobeta(S, k, v, beta, alpha, kda):
+    Sd = dr.decay(S, alpha, kda)
+    d = v - np.einsum('...ij,...i->...j', Sd, k)
+    return Sd + np.einsum('...i,...j->...ij', k, d), d
+
+
+def _tu_pred_undecayed(S, k, v, beta, alpha, kda):
+    Sd = dr.decay(S, alpha, kda)
+    d = np.asarray(beta)[..., None] * (v - np.einsum('...ij,...i->...j', S, k))
+    return Sd + np.einsum('...i,...j->...ij', k, d), d
+
+
+def _tu_decay_after(S, k, v, beta, alpha, kda):
+    d = np.asarray(beta)[..., None] * (v - np.einsum('...ij,...i->...j', S, k))
+    return dr.decay(S + np.einsum('...i,...j->...ij', k, d), alpha, kda), d
+
+
+def _tu_kda_columns(S, k, v, beta, alpha, kda):
+    alpha = np.asarray(alpha)
+    Sd = S * alpha[..., None, :] if kda else dr.decay(S, alpha, kda)
+    d = np.asarray(beta)[..., None] * (v - np.einsum('...ij,...i->...j', Sd, k))
+    return Sd + np.einsum('...i,...j->...ij', k, d), d
+
+
+def _readout_transposed(S, q):
+    return np.einsum('...ij,...j->...i', S, q)
+
+
+def _expand_tile(x, G):
+    return np.concatenate([x] * G, axis=-2)
+
+
+def _apply_record_nodecay(S, k, d, alpha, kda):
+    return S + np.einsum('...i,...j->...ij', k, d)
+
+
+def _fold_now_early(n, T, L):
+    return n + T >= L
+
+
+def _lazy_late(m, next_T, L):
+    return m + next_T > L + 1
+
+
+MUTANTS = {
+    'd sign flipped': [('token_update', _tu_sign)],
+    'beta dropped from d': [('token_update', _tu_nobeta)],
+    'prediction from undecayed state': [('token_update', _tu_pred_undecayed)],
+    'decay applied after the write': [('token_update', _tu_decay_after)],
+    'KDA decay on value axis': [('token_update', _tu_kda_columns)],
+    'readout transposed': [('readout', _readout_transposed)],
+    'key heads tiled, not grouped': [('expand_heads', _expand_tile)],
+    'record replay drops decay': [('apply_record', _apply_record_nodecay)],
+    'fused fold one record early': [('fold_now', _fold_now_early)],
+    'lazy fold one record late': [('lazy_fold', _lazy_late)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, monkeypatch):
+    for attr, fn in MUTANTS[name]:
+        for mod in (dr, rp):
+            if hasattr(mod, attr):
+                monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all='ignore'):
+                pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin rejects the mutant '{name}'"
