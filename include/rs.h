@@ -1,0 +1,185 @@
+/*
+ * rs.h -- ReplaySSM decode / speculative verify for Gated DeltaNet (GDN) and KDA layers
+ * on AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ or torch types.
+ *
+ * The method (from three public pull-request pages):
+ *   - LightLLM, "feat: add ReplaySSM state modes for GDN and KDA" (PR description; commit
+ *     messages on lazy compaction, the on-device overflow decision, the cursor kernel,
+ *     the shared cursor advanced after the last layer, fp32 delta history, the key-group
+ *     fold barrier and program order);
+ *   - vLLM, "[Feature][MRV2] Enable Qwen3.5 GDN ReplaySSM standard decode" (Overview,
+ *     Claims: no GPU-to-CPU reads, persistent graph buffers);
+ *   - sglang, GDN ReplaySSM spec verify for DFLASH/DSPARK (commit 1: ring length check and
+ *     null state slots; commit 3: causal terms selected, commit loads masked; commit 4:
+ *     the ring commit folds the accepted window; commit 5: history skipped when
+ *     write_pos is 0; Modifications; Behavior changes).
+ *
+ * The recurrence (gated delta rule; KDA when the decay is a vector over dk), with the
+ * state stored as S[dk][dv] per value head:
+ *     S' = alpha (.) S        (GDN: scalar alpha; KDA: key row i scaled by alpha[i])
+ *     d  = beta * (v - S'^T k)            the "delta", kept in fp32 history
+ *     S  = S' + k d^T,        o = S^T q  (post-update state, no extra scale)
+ * Value head h reads key head h / (hv / hk).
+ *
+ * ReplaySSM: the canonical state S of a slot stays in place.  A verify of T draft tokens
+ * replays the slot's committed history records (k, d, alpha) over S without writing S,
+ * and appends the T draft records to the slot's ring at [write_pos, write_pos + T).  The
+ * per-slot cursor counts committed records; it is shared by every layer and advanced
+ * once per step, after the last layer, by rs_cursor_advance.  When a verify's window
+ * would overflow the ring (cursor + T > L) the verify first folds the whole committed
+ * prefix into S in-kernel and writes its window at 0.  rs_commit_fold folds at commit
+ * time by policy.
+ *
+ * Ownership and execution.  The caller owns every buffer (contiguous, row-major, device
+ * memory, 16-byte aligned).  The library allocates nothing, keeps no state between calls
+ * and is reentrant.  Every call validates its arguments on the host, enqueues kernels on
+ * the given stream and returns; it never synchronises and never copies device data to
+ * the host, so a whole decode step can be captured in a HIP graph.
+ *
+ * Device-side contract (not checkable without a sync): live slots in slot_idx are
+ * distinct; 0 <= accept_len <= T; 0 <= cursor <= L; a slot restored from a checkpoint
+ * or written by prefill has cursor 0 (LightLLM: the restored slot's replay cursor is
+ * cleared); each verify of a layer is followed by one rs_cursor_advance before that
+ * layer's next verify.  For memory safety the kernels clamp out-of-contract values:
+ * slots >= num_slots are treated as null, cursors are clamped to [0, L] and accept
+ * lengths to [0, T].
+ */
+#ifndef RS_H_
+#define RS_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RS_OK = 0,
+    RS_E_NULLPTR = 1,         /* a required pointer is NULL */
+    RS_E_SHAPE = 2,           /* unsupported or inconsistent dimensions */
+    RS_E_DTYPE = 3,           /* unsupported dtype */
+    RS_E_RING_TOO_SMALL = 4,  /* ring_cap < T: the ring cannot hold the draft window */
+    RS_E_LAUNCH = 5           /* the kernel launch failed (hipGetLastError) */
+} rs_status;
+
+typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
+
+/* Fold policy applied by rs_cursor_advance (sglang commit 4; LightLLM force_compress). */
+typedef enum {
+    RS_FOLD_NONE = 0,          /* never fold at commit; verify folds in-kernel on overflow */
+    RS_FOLD_EVERY_COMMIT = 1,  /* fold every accepted window at commit */
+    RS_FOLD_LAZY = 2,          /* fold when the next verify (width next_T) would overflow */
+    RS_FOLD_FORCE = 3          /* fold rows in force_mask (every live row if NULL) */
+} rs_fold_policy;
+
+/* Shapes.  batch B: request rows; T: verify window, 1..16; hk, hv: key and value heads
+ * (hv % hk == 0; KDA needs hv == hk); dk in {16,32,...,256} and dv a multiple of 16;
+ * ring_cap L >= T, L <= 256; num_slots: size of the slot pools; act_dtype: q, k, v, beta,
+ * gate and ring keys; state_dtype: S.  tile_v: value columns per workgroup (16, 32, 64 or
+ * 128, dividing dv), or 0 for the library's choice. */
+typedef struct {
+    int32_t batch, T, hk, hv, dk, dv, ring_cap, num_slots;
+    rs_dtype act_dtype, state_dtype;
+    int32_t tile_v;
+} rs_dims;
+
+/*
+ * rs_gdn_verify -- verify (T >= 1) or decode (T == 1) of one GDN layer.
+ *   q, k        [B*T, hk, dk]  act dtype (token t of row r at r*T + t)
+ *   v           [B*T, hv, dv]  act dtype
+ *   beta, gate  [B*T, hv]      act dtype; gate is the linear decay alpha in (0, 1]
+ *   state       [num_slots, hv, dk, dv] state dtype; written only for rows that fold
+ *               (bf16: round-to-nearest-even on every write)
+ *   ring_k      [num_slots, L, hk, dk] act dtype  (exact copies of k)
+ *   ring_d      [num_slots, L, hv, dv] fp32        (deltas)
+ *   ring_g      [num_slots, L, hv]     fp32        (exact upcasts of gate)
+ *   cursor      [num_slots] int32, read only
+ *   slot_idx    [B] int32; a negative slot is a null row: nothing is read or written
+ *   out         [B*T, hv, dv] fp32; null rows are not written
+ *   write_pos_out [B] int32 or NULL: write_pos of each live row (0 after a fold)
+ *   group_counter [B, hk] int32 workspace, zeroed once by the caller; every call leaves
+ *               it zeroed.  It orders the fused fold's rewrite of the shared ring keys
+ *               and gates after every workgroup of the key group has read them (LightLLM
+ *               commit on the key-group fold barrier), with no spinning.
+ * Rows folding in-kernel: S <- fold(S, ring[0:cursor]), then write_pos = 0.  Otherwise
+ * write_pos = cursor and the history [0, cursor) is replayed without writing S.  The T
+ * draft records go to ring rows [write_pos, write_pos + T).  Causal terms are selected,
+ * never multiplied by zero, so non-finite inputs at draft t reach no output before t.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_LAUNCH.
+ */
+rs_status rs_gdn_verify(const rs_dims* dims,
+                        const void* q, const void* k, const void* v,
+                        const void* beta, const void* gate,
+                        void* state, void* ring_k, float* ring_d, float* ring_g,
+                        const int32_t* cursor, const int32_t* slot_idx,
+                        float* out, int32_t* write_pos_out, int32_t* group_counter,
+                        hipStream_t stream);
+
+/*
+ * rs_kda_verify -- as rs_gdn_verify for KDA (LightLLM: KDA gets the same windowed
+ * reconstruction): hv == hk, the decay is per key channel.
+ *   gate    [B*T, hv, dk] act dtype
+ *   ring_g  [num_slots, L, hv, dk] fp32
+ * Every other argument as for rs_gdn_verify.
+ */
+rs_status rs_kda_verify(const rs_dims* dims,
+                        const void* q, const void* k, const void* v,
+                        const void* beta, const void* gate,
+                        void* state, void* ring_k, float* ring_d, float* ring_g,
+                        const int32_t* cursor, const int32_t* slot_idx,
+                        float* out, int32_t* write_pos_out, int32_t* group_counter,
+                        hipStream_t stream);
+
+/*
+ * rs_cursor_advance -- once per step, after every layer's verify (LightLLM: the shared
+ * cursor is advanced only after the last layer; MTP verify trims the rejected tail).
+ * For each live row r with slot s: write_pos = (cursor[s] + T > L) ? 0 : cursor[s];
+ * m = write_pos + accept_len[r]; fold_len[s] = m if the policy folds the row, else 0;
+ * cursor[s] = fold_len[s] ? 0 : m.  LAZY folds when m + next_T > L; FORCE folds rows with
+ * force_mask[r] != 0 (every live row when force_mask is NULL).  Null rows are skipped
+ * (sglang commit 1).
+ *   cursor [num_slots] int32 (in/out); fold_len [num_slots] int32 (out, live slots only)
+ *   slot_idx [B] int32; accept_len [B] int32 in [0, T]; force_mask [B] uint8 or NULL
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_RING_TOO_SMALL, RS_E_LAUNCH.
+ */
+rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_len,
+                            const int32_t* slot_idx, const int32_t* accept_len,
+                            rs_fold_policy policy, int32_t next_T,
+                            const uint8_t* force_mask, hipStream_t stream);
+
+/*
+ * rs_commit_fold -- compact commit: S[s] <- fold(S[s], ring[s, 0:fold_len[s]]) for each
+ * live row with fold_len > 0.  Reads fold_len, never the cursor, so layers sharing one
+ * cursor all fold the same prefix after it was reset (sglang commits 3 and 4: the ring
+ * loads are masked to the committed history).  bf16 states are rounded once, on write.
+ *   is_kda: 0 = GDN (ring_g [num_slots, L, hv]), 1 = KDA (ring_g [num_slots, L, hv, dk])
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_LAUNCH.
+ */
+rs_status rs_commit_fold(const rs_dims* dims, int is_kda, void* state, const void* ring_k,
+                         const float* ring_d, const float* ring_g, const int32_t* fold_len,
+                         const int32_t* slot_idx, hipStream_t stream);
+
+/*
+ * rs_materialize -- the accepted state fold(S[s], ring[s, 0:cursor[s]]) of each live row
+ * into out_state [B, hv, dk, dv] fp32 (LightLLM: accepted-state materialization; a
+ * read-only fold).  S, rings and cursors are not modified; null rows are not written.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_LAUNCH.
+ */
+rs_status rs_materialize(const rs_dims* dims, int is_kda, const void* state,
+                         const void* ring_k, const float* ring_d, const float* ring_g,
+                         const int32_t* cursor, const int32_t* slot_idx, float* out_state,
+                         hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* rs_status_str(rs_status status);
+
+/* Workgroup count and dynamic LDS bytes the verify launches for these dims, for
+ * profiling and tests.  Returns RS_OK or the validation error. */
+rs_status rs_verify_launch_info(const rs_dims* dims, int is_kda, int32_t* tile_v,
+                                int32_t* workgroups, int32_t* lds_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RS_H_ */

@@ -1,0 +1,191 @@
+"""ReplaySSM decode / speculative verify for GDN and KDA layers on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/rs.h (librs.so, built in-tree by
+``linear_attention_recurrent_rs_amd.build``).  Every function here marshals torch
+tensors into pointers and sizes and calls the library; all computation runs in the HIP
+kernels.  Before a call it checks that each tensor lives on the GPU, is contiguous and
+has the element count and dtype the dimensions imply, so a wrong tensor becomes an
+exception instead of an out-of-bounds device access.  There is no fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'commit_fold',
+           'materialize', 'verify_launch_info', 'library_path', 'F32', 'BF16',
+           'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE']
+
+F32, BF16 = 0, 1
+FOLD_NONE, FOLD_EVERY_COMMIT, FOLD_LAZY, FOLD_FORCE = 0, 1, 2, 3
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'librs.so')
+
+
+class RSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib().rs_status_str(status).decode()}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """rs_dims: batch, T, hk, hv, dk, dv, ring_cap, num_slots, act_dtype, state_dtype, tile_v."""
+    _fields_ = [('batch', ctypes.c_int32), ('T', ctypes.c_int32), ('hk', ctypes.c_int32),
+                ('hv', ctypes.c_int32), ('dk', ctypes.c_int32), ('dv', ctypes.c_int32),
+                ('ring_cap', ctypes.c_int32), ('num_slots', ctypes.c_int32),
+                ('act_dtype', ctypes.c_int), ('state_dtype', ctypes.c_int),
+                ('tile_v', ctypes.c_int32)]
+
+    def __repr__(self):
+        return 'Dims(' + ', '.join(f'{f}={getattr(self, f)}' for f, _ in self._fields_) + ')'
+
+
+_LIB = None
+_P = ctypes.c_void_p
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run "
+                               "`python -m linear_attention_recurrent_rs_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        dp = ctypes.POINTER(Dims)
+        verify_args = [dp] + [_P] * 14 + [_P]
+        for name in ('rs_gdn_verify', 'rs_kda_verify'):
+            getattr(lib, name).argtypes = verify_args
+            getattr(lib, name).restype = ctypes.c_int
+        lib.rs_cursor_advance.argtypes = [dp, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int32, _P, _P]
+        lib.rs_cursor_advance.restype = ctypes.c_int
+        lib.rs_commit_fold.argtypes = [dp, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P]
+        lib.rs_commit_fold.restype = ctypes.c_int
+        lib.rs_materialize.argtypes = [dp, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]
+        lib.rs_materialize.restype = ctypes.c_int
+        lib.rs_status_str.argtypes = [ctypes.c_int]
+        lib.rs_status_str.restype = ctypes.c_char_p
+        lib.rs_verify_launch_info.argtypes = [dp, ctypes.c_int, _P, _P, _P]
+        lib.rs_verify_launch_info.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, numel: int, dtype: torch.dtype,
+         optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RSError(status, where)
+
+
+def _verify(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+            slot_idx, out, write_pos_out, group_counter, stream):
+    at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
+    BT, S, L = d.batch * d.T, d.num_slots, d.ring_cap
+    g_per = d.hv * d.dk if kda else d.hv
+    args = [
+        _ptr(q, 'q', BT * d.hk * d.dk, at), _ptr(k, 'k', BT * d.hk * d.dk, at),
+        _ptr(v, 'v', BT * d.hv * d.dv, at), _ptr(beta, 'beta', BT * d.hv, at),
+        _ptr(gate, 'gate', BT * g_per, at),
+        _ptr(state, 'state', S * d.hv * d.dk * d.dv, st),
+        _ptr(ring_k, 'ring_k', S * L * d.hk * d.dk, at),
+        _ptr(ring_d, 'ring_d', S * L * d.hv * d.dv, torch.float32),
+        _ptr(ring_g, 'ring_g', S * L * g_per, torch.float32),
+        _ptr(cursor, 'cursor', S, torch.int32), _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+        _ptr(out, 'out', BT * d.hv * d.dv, torch.float32),
+        _ptr(write_pos_out, 'write_pos_out', d.batch, torch.int32, optional=True),
+        _ptr(group_counter, 'group_counter', d.batch * d.hk, torch.int32),
+    ]
+    fn = _lib().rs_kda_verify if kda else _lib().rs_gdn_verify
+    _check(fn(ctypes.byref(d), *args, _stream(stream)), 'rs_kda_verify' if kda else 'rs_gdn_verify')
+
+
+def gdn_verify(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx,
+               out, write_pos_out=None, group_counter=None, stream=None):
+    """rs_gdn_verify: one GDN layer's verify (decode when T == 1)."""
+    _verify(False, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx, out,
+            write_pos_out, group_counter, stream)
+
+
+def kda_verify(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx,
+               out, write_pos_out=None, group_counter=None, stream=None):
+    """rs_kda_verify: one KDA layer's verify (per-channel decay)."""
+    _verify(True, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx, out,
+            write_pos_out, group_counter, stream)
+
+
+def cursor_advance(d: Dims, cursor, fold_len, slot_idx, accept_len, policy: int = FOLD_NONE,
+                   next_T: int = 0, force_mask=None, stream=None):
+    """rs_cursor_advance: once per step, after every layer's verify."""
+    args = [_ptr(cursor, 'cursor', d.num_slots, torch.int32),
+            _ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    fm = _ptr(force_mask, 'force_mask', d.batch, torch.uint8, optional=True)
+    _check(_lib().rs_cursor_advance(ctypes.byref(d), *args, int(policy), int(next_T), fm,
+                                    _stream(stream)), 'rs_cursor_advance')
+
+
+def _fold_ptrs(d: Dims, kda: bool, state, ring_k, ring_d, ring_g):
+    at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
+    S, L = d.num_slots, d.ring_cap
+    g_per = d.hv * d.dk if kda else d.hv
+    return [_ptr(state, 'state', S * d.hv * d.dk * d.dv, st),
+            _ptr(ring_k, 'ring_k', S * L * d.hk * d.dk, at),
+            _ptr(ring_d, 'ring_d', S * L * d.hv * d.dv, torch.float32),
+            _ptr(ring_g, 'ring_g', S * L * g_per, torch.float32)]
+
+
+def commit_fold(d: Dims, kda: bool, state, ring_k, ring_d, ring_g, fold_len, slot_idx,
+                stream=None):
+    """rs_commit_fold: fold ring[0:fold_len[s]] into S[s] for live rows."""
+    p = _fold_ptrs(d, kda, state, ring_k, ring_d, ring_g)
+    _check(_lib().rs_commit_fold(ctypes.byref(d), int(kda), *p,
+                                 _ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+                                 _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+                                 _stream(stream)), 'rs_commit_fold')
+
+
+def materialize(d: Dims, kda: bool, state, ring_k, ring_d, ring_g, cursor, slot_idx, out_state,
+                stream=None):
+    """rs_materialize: fold(S[s], ring[s, 0:cursor[s]]) into out_state [B, hv, dk, dv] fp32."""
+    p = _fold_ptrs(d, kda, state, ring_k, ring_d, ring_g)
+    _check(_lib().rs_materialize(ctypes.byref(d), int(kda), *p,
+                                 _ptr(cursor, 'cursor', d.num_slots, torch.int32),
+                                 _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+                                 _ptr(out_state, 'out_state', d.batch * d.hv * d.dk * d.dv,
+                                      torch.float32),
+                                 _stream(stream)), 'rs_materialize')
+
+
+def verify_launch_info(d: Dims, kda: bool = False):
+    """(tile_v, workgroups, lds_bytes) the verify launches with for these dims."""
+    tv, wg, lds = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib().rs_verify_launch_info(ctypes.byref(d), int(kda), ctypes.byref(tv),
+                                        ctypes.byref(wg), ctypes.byref(lds)),
+           'rs_verify_launch_info')
+    return tv.value, wg.value, lds.value

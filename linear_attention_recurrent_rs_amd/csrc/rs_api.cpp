@@ -1,0 +1,195 @@
+// C ABI of the ReplaySSM library: host-side validation, tile choice and kernel launch.
+// Every entry point enqueues on the caller's stream and returns without synchronising.
+#include "rs.h"
+#include "rs_internal.h"
+
+namespace {
+
+constexpr int kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
+bool dtype_ok(rs_dtype d) { return d == RS_F32 || d == RS_BF16; }
+int dbytes(rs_dtype d) { return d == RS_BF16 ? 2 : 4; }
+
+rs_status check_common(const rs_dims* d, bool need_T) {
+  if (!d) return RS_E_NULLPTR;
+  if (!dtype_ok(d->act_dtype) || !dtype_ok(d->state_dtype)) return RS_E_DTYPE;
+  if (d->batch < 0 || d->hk < 1 || d->hv < 1 || d->hv % d->hk != 0) return RS_E_SHAPE;
+  if (d->dk < 16 || d->dk > 256 || d->dk % 16 != 0) return RS_E_SHAPE;
+  if (d->dv < 16 || d->dv % 16 != 0) return RS_E_SHAPE;
+  if (d->num_slots < 1 || d->ring_cap < 1 || d->ring_cap > 256) return RS_E_SHAPE;
+  if (need_T && (d->T < 1 || d->T > 16)) return RS_E_SHAPE;
+  if (need_T && d->ring_cap < d->T) return RS_E_RING_TOO_SMALL;
+  if (d->tile_v != 0) {
+    if (d->tile_v != 16 && d->tile_v != 32 && d->tile_v != 64 && d->tile_v != 128) return RS_E_SHAPE;
+    if (d->dv % d->tile_v != 0) return RS_E_SHAPE;
+  }
+  return RS_OK;
+}
+
+int tmax_of(int T) {
+  int t = 1;
+  while (t < T) t <<= 1;
+  return t;
+}
+
+// Value columns per workgroup: the caller's tile, else the widest of 64/32/16 dividing dv.
+int choose_bv(const rs_dims* d) {
+  if (d->tile_v) return d->tile_v;
+  if (d->dv % 64 == 0) return 64;
+  if (d->dv % 32 == 0) return 32;
+  return 16;
+}
+
+rs_status verify_plan(const rs_dims* d, bool kda, int* bv, int* tmax, rs::LdsLayout* lay) {
+  rs_status st = check_common(d, true);
+  if (st != RS_OK) return st;
+  if (kda && d->hv != d->hk) return RS_E_SHAPE;
+  *tmax = tmax_of(d->T);
+  *bv = choose_bv(d);
+  *lay = rs::verify_layout(kda, dbytes(d->state_dtype), *bv, *tmax, d->T, d->dk, d->ring_cap);
+  while (lay->total > kMaxLds && d->tile_v == 0 && *bv > 16) {
+    *bv /= 2;
+    *lay = rs::verify_layout(kda, dbytes(d->state_dtype), *bv, *tmax, d->T, d->dk, d->ring_cap);
+  }
+  if (lay->total > kMaxLds) return RS_E_SHAPE;
+  return RS_OK;
+}
+
+rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, const void* v,
+                      const void* beta, const void* gate, void* state, void* ring_k,
+                      float* ring_d, float* ring_g, const int32_t* cursor,
+                      const int32_t* slot_idx, float* out, int32_t* write_pos_out,
+                      int32_t* group_counter, hipStream_t stream) {
+  int bv = 0, tmax = 0;
+  rs::LdsLayout lay{};
+  rs_status st = verify_plan(d, kda, &bv, &tmax, &lay);
+  if (st != RS_OK) return st;
+  if (d->batch == 0) return RS_OK;
+  if (!q || !k || !v || !beta || !gate || !state || !ring_k || !ring_d || !ring_g || !cursor ||
+      !slot_idx || !out || !group_counter)
+    return RS_E_NULLPTR;
+  rs::VerifyArgs a{};
+  a.B = d->batch; a.T = d->T; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
+  a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
+  a.nblocks = d->batch * d->hv * a.NV;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate;
+  a.state = state; a.ring_k = ring_k; a.ring_d = ring_d; a.ring_g = ring_g;
+  a.cursor = cursor; a.slot_idx = slot_idx; a.out = out; a.write_pos_out = write_pos_out;
+  a.group_counter = group_counter; a.lay = lay;
+  hipError_t e = rs::launch_verify(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv,
+                                   tmax, a, stream);
+  return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* state_out,
+                    const void* ring_k, const float* ring_d, const float* ring_g,
+                    const int32_t* nrec, const int32_t* slot_idx, bool materialize,
+                    hipStream_t stream) {
+  rs_status st = check_common(d, false);
+  if (st != RS_OK) return st;
+  const bool kda = is_kda != 0;
+  if (kda && d->hv != d->hk) return RS_E_SHAPE;
+  int bv = choose_bv(d);
+  rs::LdsLayout lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
+  while (lay.total > kMaxLds && d->tile_v == 0 && bv > 16) {
+    bv /= 2;
+    lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
+  }
+  if (lay.total > kMaxLds) return RS_E_SHAPE;
+  if (d->batch == 0) return RS_OK;
+  if (!state_in || !state_out || !ring_k || !ring_d || !ring_g || !nrec || !slot_idx)
+    return RS_E_NULLPTR;
+  rs::FoldArgs a{};
+  a.B = d->batch; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv; a.L = d->ring_cap;
+  a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
+  a.nblocks = d->batch * d->hv * a.NV;
+  a.state_in = state_in; a.state_out = state_out; a.ring_k = ring_k; a.ring_d = ring_d;
+  a.ring_g = ring_g; a.nrec = nrec; a.slot_idx = slot_idx; a.lay = lay;
+  hipError_t e = rs::launch_fold(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv,
+                                 materialize, a, stream);
+  return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+rs_status rs_gdn_verify(const rs_dims* dims, const void* q, const void* k, const void* v,
+                        const void* beta, const void* gate, void* state, void* ring_k,
+                        float* ring_d, float* ring_g, const int32_t* cursor,
+                        const int32_t* slot_idx, float* out, int32_t* write_pos_out,
+                        int32_t* group_counter, hipStream_t stream) {
+  return verify_impl(false, dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                     slot_idx, out, write_pos_out, group_counter, stream);
+}
+
+rs_status rs_kda_verify(const rs_dims* dims, const void* q, const void* k, const void* v,
+                        const void* beta, const void* gate, void* state, void* ring_k,
+                        float* ring_d, float* ring_g, const int32_t* cursor,
+                        const int32_t* slot_idx, float* out, int32_t* write_pos_out,
+                        int32_t* group_counter, hipStream_t stream) {
+  return verify_impl(true, dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                     slot_idx, out, write_pos_out, group_counter, stream);
+}
+
+rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_len,
+                            const int32_t* slot_idx, const int32_t* accept_len,
+                            rs_fold_policy policy, int32_t next_T, const uint8_t* force_mask,
+                            hipStream_t stream) {
+  if (!dims) return RS_E_NULLPTR;
+  if (dims->batch < 0 || dims->T < 1 || dims->T > 16 || dims->num_slots < 1 ||
+      dims->ring_cap < 1 || dims->ring_cap > 256)
+    return RS_E_SHAPE;
+  if (dims->ring_cap < dims->T) return RS_E_RING_TOO_SMALL;
+  if (policy < RS_FOLD_NONE || policy > RS_FOLD_FORCE) return RS_E_SHAPE;
+  if (policy == RS_FOLD_LAZY && (next_T < 1 || next_T > 16)) return RS_E_SHAPE;
+  if (dims->batch == 0) return RS_OK;
+  if (!cursor || !fold_len || !slot_idx || !accept_len) return RS_E_NULLPTR;
+  rs::AdvanceArgs a{};
+  a.B = dims->batch; a.T = dims->T; a.L = dims->ring_cap; a.num_slots = dims->num_slots;
+  a.policy = int(policy); a.next_T = next_T;
+  a.cursor = cursor; a.fold_len = fold_len; a.slot_idx = slot_idx; a.accept = accept_len;
+  a.force_mask = force_mask;
+  return rs::launch_advance(a, stream) == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+rs_status rs_commit_fold(const rs_dims* dims, int is_kda, void* state, const void* ring_k,
+                         const float* ring_d, const float* ring_g, const int32_t* fold_len,
+                         const int32_t* slot_idx, hipStream_t stream) {
+  return fold_impl(dims, is_kda, state, state, ring_k, ring_d, ring_g, fold_len, slot_idx,
+                   false, stream);
+}
+
+rs_status rs_materialize(const rs_dims* dims, int is_kda, const void* state, const void* ring_k,
+                         const float* ring_d, const float* ring_g, const int32_t* cursor,
+                         const int32_t* slot_idx, float* out_state, hipStream_t stream) {
+  if (out_state == nullptr && dims && dims->batch > 0) return RS_E_NULLPTR;
+  return fold_impl(dims, is_kda, state, out_state, ring_k, ring_d, ring_g, cursor, slot_idx,
+                   true, stream);
+}
+
+const char* rs_status_str(rs_status s) {
+  switch (s) {
+    case RS_OK: return "RS_OK";
+    case RS_E_NULLPTR: return "RS_E_NULLPTR: a required pointer is NULL";
+    case RS_E_SHAPE: return "RS_E_SHAPE: unsupported or inconsistent dimensions";
+    case RS_E_DTYPE: return "RS_E_DTYPE: unsupported dtype";
+    case RS_E_RING_TOO_SMALL: return "RS_E_RING_TOO_SMALL: ring_cap < T";
+    case RS_E_LAUNCH: return "RS_E_LAUNCH: kernel launch failed";
+  }
+  return "unknown rs_status";
+}
+
+rs_status rs_verify_launch_info(const rs_dims* dims, int is_kda, int32_t* tile_v,
+                                int32_t* workgroups, int32_t* lds_bytes) {
+  int bv = 0, tmax = 0;
+  rs::LdsLayout lay{};
+  rs_status st = verify_plan(dims, is_kda != 0, &bv, &tmax, &lay);
+  if (st != RS_OK) return st;
+  if (tile_v) *tile_v = bv;
+  if (workgroups) *workgroups = dims->batch * dims->hv * (dims->dv / bv);
+  if (lds_bytes) *lds_bytes = lay.total;
+  return RS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers shared by the ReplaySSM kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rs {
+
+constexpr int kThreads = 256;   // threads per workgroup: 4 waves of 64
+constexpr int kWaves = 4;
+constexpr int kXcds = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16;
+
+// ------------------------------------------------------------------ number formats
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16 bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return bf16_rne(x); }
+
+// The value a state element holds once stored in type T (identity for fp32).
+template <typename T> __device__ __forceinline__ float stored_value(float x) {
+  return to_f32(from_f32<T>(x));
+}
+
+// Four consecutive elements as floats / from floats.
+__device__ __forceinline__ f4 load4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 load4(const bf16* p) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  f4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xffff0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
+__device__ __forceinline__ void store4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, f4 v) {
+  uint2 u;
+  u.x = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+  u.y = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+template <typename T> __device__ __forceinline__ f4 round4(f4 v) {
+  f4 r;
+  r[0] = stored_value<T>(v[0]); r[1] = stored_value<T>(v[1]);
+  r[2] = stored_value<T>(v[2]); r[3] = stored_value<T>(v[3]);
+  return r;
+}
+
+// ------------------------------------------------------------------ LDS state tile
+// A [rows x bv] tile of element type T, stored as 16-byte chunks.  Chunk c of row r sits
+// at chunk slot (c ^ (r % cpr)) of that row (cpr = chunks per row, a power of two), so
+// that 16 lanes reading one chunk column of 16 consecutive rows, or 16 consecutive chunks
+// of one row, hit distinct bank groups.
+template <typename T, int BV>
+struct Tile {
+  static constexpr int kCpr = BV * int(sizeof(T)) / 16;   // chunks per row
+  static constexpr int kEpc = 16 / int(sizeof(T));         // elements per chunk
+  static_assert(kCpr >= 1 && (kCpr & (kCpr - 1)) == 0, "chunks per row must be 2^n");
+  // element offset of (row r, column c), c % 4 == 0 (four columns never straddle chunks)
+  __device__ __forceinline__ static int at(int r, int c) {
+    int chunk = c / kEpc;
+    return r * BV + ((chunk ^ (r & (kCpr - 1))) * kEpc) + (c % kEpc);
+  }
+  // global chunk held by linear LDS chunk slot p (inverse of the swizzle)
+  __device__ __forceinline__ static void slot_source(int p, int& r, int& chunk) {
+    r = p / kCpr;
+    chunk = (p % kCpr) ^ (r & (kCpr - 1));
+  }
+};
+
+// ------------------------------------------------------------------ grid order
+// Hardware hands workgroup p to XCD p % 8.  Return a logical index so that each XCD
+// receives one contiguous range of logical indices (neighbouring value heads of one
+// request, which share key heads and history keys, then share an L2).  Bijective on
+// [0, n) for any n.
+__device__ __forceinline__ int xcd_remap(int p, int n) {
+  int xcd = p % kXcds, idx = p / kXcds;
+  int per = n / kXcds, extra = n % kXcds;
+  return xcd * per + (xcd < extra ? xcd : extra) + idx;
+}
+
+// ------------------------------------------------------------------ MFMA
+// D(16x16) += A(16x4) B(4x16), fp32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
+// it holds D[4*(l/16)+i][l%16] in element i of the accumulator.
+__device__ __forceinline__ f4 mfma_16x16x4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l writes lds_wave_base + 16*l.
+__device__ __forceinline__ void load_lds_16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+}  // namespace rs

@@ -1,0 +1,123 @@
+// Host <-> device launch structures shared by the kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rs {
+
+// Byte offsets of the regions of a workgroup's dynamic LDS (all 16-byte aligned).
+struct LdsLayout {
+  int tile_raw;   // state tile as stored [dk x bv], swizzled
+  int tile32;     // fp32 tile after history replay or fold (aliases tile_raw for fp32 S)
+  int khat;       // history keys scaled by their suffix decay [L4 x dk] fp32
+  int dhist;      // history deltas of this tile's columns [L4 x bv] fp32
+  int hg;         // history gates [L] (GDN) or [L x dk] (KDA) fp32
+  int xraw;       // window q_t, k_t as fp32 [2*tmax x xs_stride]
+  int xs;         // window q_t, k_t scaled by the in-window prefix decay [nvec_pad x xs_stride]
+  int gw;         // window gates [tmax] (GDN) or [tmax x dk] (KDA)
+  int bw;         // window betas [tmax]
+  int gam;        // total history decay per key channel [dk]
+  int P;          // readout H^T xs [2*tmax x bv]
+  int red;        // cross-wave reduction scratch [4 x vpp x bv]
+  int Am;         // beta_t (k_t . dec(u,t) k_u), u < t  [tmax x tmax]
+  int Qm;         // q_t . dec(u,t) k_u, u <= t          [tmax x tmax]
+  int flags;      // [0]: this workgroup is the last of its key group to arrive
+  int total;
+  int xs_stride;  // dk + 4 floats
+  int nvec_pad;   // 2T rounded up to the readout batch
+};
+
+struct VerifyArgs {
+  int B, T, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* beta;
+  const void* gate;
+  void* state;
+  void* ring_k;
+  float* ring_d;
+  float* ring_g;
+  const int32_t* cursor;
+  const int32_t* slot_idx;
+  float* out;
+  int32_t* write_pos_out;
+  int32_t* group_counter;
+  LdsLayout lay;
+};
+
+struct FoldArgs {
+  int B, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
+  const void* state_in;     // S (read)
+  void* state_out;          // S (commit fold) or the fp32 materialize output
+  const void* ring_k;
+  const float* ring_d;
+  const float* ring_g;
+  const int32_t* nrec;      // fold_len (commit) or cursor (materialize), per slot
+  const int32_t* slot_idx;
+  LdsLayout lay;
+};
+
+struct AdvanceArgs {
+  int B, T, L, num_slots, policy, next_T;
+  int32_t* cursor;
+  int32_t* fold_len;
+  const int32_t* slot_idx;
+  const int32_t* accept;
+  const uint8_t* force_mask;
+};
+
+// Readout batch: window vectors (2T of them) processed per pass over the tile.
+inline int readout_vpp(int tmax) { return 2 * tmax < 8 ? 2 * tmax : 8; }
+
+inline LdsLayout verify_layout(bool kda, int st_bytes, int bv, int tmax, int T, int dk, int L) {
+  auto al = [](int x) { return (x + 15) & ~15; };
+  const int vpp = readout_vpp(tmax);
+  LdsLayout l{};
+  int o = 0;
+  l.tile_raw = o; o += al(dk * bv * st_bytes);
+  if (st_bytes == 4) { l.tile32 = l.tile_raw; } else { l.tile32 = o; o += al(dk * bv * 4); }
+  const int L4 = (L + 3) & ~3;
+  l.khat = o; o += al(L4 * dk * 4);
+  l.dhist = o; o += al(L4 * bv * 4);
+  l.hg = o; o += al(kda ? L * dk * 4 : L * 4);
+  l.xs_stride = dk + 4;
+  l.nvec_pad = ((2 * T + vpp - 1) / vpp) * vpp;
+  l.xraw = o; o += al(2 * tmax * l.xs_stride * 4);
+  l.xs = o; o += al(l.nvec_pad * l.xs_stride * 4);
+  l.gw = o; o += al(kda ? tmax * dk * 4 : tmax * 4);
+  l.bw = o; o += al(tmax * 4);
+  l.gam = o; o += al(dk * 4);
+  l.P = o; o += al(2 * tmax * bv * 4);
+  l.red = o; o += al(4 * vpp * bv * 4);
+  l.Am = o; o += al(tmax * tmax * 4);
+  l.Qm = o; o += al(tmax * tmax * 4);
+  l.flags = o; o += 16;
+  l.total = o;
+  return l;
+}
+
+inline LdsLayout fold_layout(bool kda, int st_bytes, int bv, int dk, int L, bool need_tile32) {
+  auto al = [](int x) { return (x + 15) & ~15; };
+  LdsLayout l{};
+  int o = 0;
+  l.tile_raw = o; o += al(dk * bv * st_bytes);
+  if (st_bytes == 4 || !need_tile32) { l.tile32 = l.tile_raw; } else { l.tile32 = o; o += al(dk * bv * 4); }
+  const int L4 = (L + 3) & ~3;
+  l.khat = o; o += al(L4 * dk * 4);
+  l.dhist = o; o += al(L4 * bv * 4);
+  l.hg = o; o += al(kda ? L * dk * 4 : L * 4);
+  l.gam = o; o += al(dk * 4);
+  l.total = o;
+  return l;
+}
+
+// Launchers (defined in rs_kernels.hip).  Return hipGetLastError() after the launch.
+hipError_t launch_verify(bool kda, int act_bf16, int state_bf16, int bv, int tmax,
+                         const VerifyArgs& a, hipStream_t s);
+hipError_t launch_fold(bool kda, int act_bf16, int state_bf16, int bv, bool materialize,
+                       const FoldArgs& a, hipStream_t s);
+hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
+
+}  // namespace rs

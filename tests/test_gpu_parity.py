@@ -1,0 +1,142 @@
+"""GPU parity: the HIP library against the fp64 oracle, through the C ABI.
+
+Reduced-size copies of the five workloads compare every row, every step: outputs (finite
+oracle positions; accepted positions must be finite on both sides), states and committed
+ring deltas within the tolerance (1e-4 of the largest magnitude for fp32 states, 5e-3 for
+bf16), ring keys/gates, write_pos, cursors and fold_len bit-exact, null rows untouched,
+unused slots untouched.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+REDUCED = {
+    # decode: 17 rows with staggered cursors 0..15,0 (two null), 2 key / 4 value heads
+    'c1': W.CONFIGS['c1'].with_(B=17, null_rows=2, hk=2, hv=4, steps=20),
+    # spec verify, bf16 state, every-commit fold, NaN/Inf in rejected drafts
+    'c2': W.CONFIGS['c2'].with_(B=7, hk=2, hv=4),
+    # KDA, per-channel decay, fused folds
+    'c3': W.CONFIGS['c3'].with_(B=5, hk=3, hv=3),
+    # large ring, 4 layers sharing one cursor, forced commit folds
+    'c4': W.CONFIGS['c4'].with_(B=5, hk=2, hv=4),
+}
+
+
+def _run(cfg, rows=None, steps=None, tile_v=0):
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init, tile_v=tile_v)
+    o = H.OracleRun(cfg, init, rows=rows)
+    rows = list(range(cfg.B)) if rows is None else rows
+    worst = H.StepReport()
+    for j in range(cfg.steps if steps is None else steps):
+        acc, ins, pol, next_T = H.step_data(cfg, j)
+        print(f'[{cfg.name}] step {j} policy {pol}', flush=True)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T)
+        o_outs, o_wps = o.step(acc, ins, pol, next_T)
+        rep = H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, acc, rows, init)
+        worst.out_err = max(worst.out_err, rep.out_err)
+        worst.state_err = max(worst.state_err, rep.state_err)
+        worst.ring_d_err = max(worst.ring_d_err, rep.ring_d_err)
+    H.check_untouched(cfg, g, init)
+    # the accepted state, read-only
+    for l in range(cfg.layers):
+        m = g.materialize(l).cpu().numpy()
+        live = [r for r in rows if init.slots[r] >= 0]
+        for r in rows:
+            if init.slots[r] < 0:
+                assert np.all(m[r] == H.SENTINEL_OUT)
+        ref = np.array([o.streams[l].H[int(init.slots[r])] for r in live])
+        err = H.rel_err(m[live], ref)
+        assert err <= H.tol_for(cfg), f'materialize error {err:.3e}'
+    print(f'[{cfg.name}] worst out {worst.out_err:.2e} state {worst.state_err:.2e} '
+          f'ring_d {worst.ring_d_err:.2e}', flush=True)
+    return g, o, init, worst
+
+
+def test_c0_against_golden():
+    cfg = W.CONFIGS['c0']
+    g, o, init, _ = _run(cfg)
+    gold = json.load(open(os.path.join(HERE, 'golden', 'c0_oracle.json')))
+    # replay the GPU run again, checking each step against the stored fixture
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init)
+    for j, st in enumerate(gold['steps']):
+        acc, ins, pol, next_T = H.step_data(cfg, j)
+        outs, wps = g.step(acc, ins, pol, next_T)
+        assert int(wps[0][0]) == st['write_pos']
+        assert int(g.cursor[gold['slot']]) == st['cursor']
+        ref = np.array(st['out'])
+        assert H.rel_err(outs[0].cpu().numpy().reshape(ref.shape), ref) <= 1e-4
+    assert sum(s['fused_fold'] for s in gold['steps']) == 2
+    S = g.S[0][gold['slot']].cpu().numpy()
+    assert H.rel_err(S, np.array(gold['S_final'])) <= 1e-4
+
+
+@pytest.mark.parametrize('name', sorted(REDUCED))
+def test_reduced_all_rows(name):
+    _run(REDUCED[name])
+
+
+@pytest.mark.parametrize('tile_v', [16, 32, 128])
+def test_tile_widths(tile_v):
+    """Every value-tile width gives the same results (C1 shape, few steps)."""
+    _run(REDUCED['c1'].with_(steps=18), tile_v=tile_v)
+
+
+def test_odd_shapes():
+    """dk=dv=16 (one 16-wide tile), dv=48 (three 16-wide tiles), dk=64, ring == window."""
+    _run(W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=16, dv=48, L=3, T=3, accept=('uniform', 0, 3),
+                               steps=10, act_dtype='bf16'))
+    _run(W.CONFIGS['c3'].with_(B=3, hk=2, hv=2, dk=64, dv=32, L=5, T=2, steps=9))
+
+
+def test_error_codes():
+    """Argument errors surface as exceptions before any kernel runs: the binding refuses
+    host tensors and wrong sizes; the library reports RS_E_RING_TOO_SMALL and RS_E_SHAPE."""
+    import linear_attention_recurrent_rs_amd as rs
+    cfg = REDUCED['c1']
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init)
+    acc, ins, pol, next_T = H.step_data(cfg, 0)
+    q, k, v, beta, gate = g.inputs_dev(ins[0])
+    args = [q, k, v, beta, gate, g.S[0], g.rk[0], g.rd[0], g.rg[0], g.cursor, g.slots, g.out,
+            g.wp, g.counter]
+    with pytest.raises(ValueError):                      # a host tensor
+        rs.gdn_verify(g.d, q.cpu(), *args[1:])
+    with pytest.raises(ValueError):                      # wrong element count
+        rs.gdn_verify(g.d, q[:-1], *args[1:])
+    small = rs.Dims(cfg.B, 4, cfg.hk, cfg.hv, cfg.dk, cfg.dv, 3, cfg.num_slots, rs.BF16, rs.F32, 0)
+    with pytest.raises(rs.RSError) as e:
+        rs.verify_launch_info(small)
+    assert e.value.status == 4                           # RS_E_RING_TOO_SMALL
+    kda = rs.Dims(cfg.B, 1, cfg.hk, cfg.hv, cfg.dk, cfg.dv, cfg.L, cfg.num_slots, rs.BF16, rs.F32, 0)
+    with pytest.raises(rs.RSError) as e:
+        rs.verify_launch_info(kda, kda=True)             # KDA needs hv == hk
+    assert e.value.status == 2
+    assert rs.verify_launch_info(g.d)[1] == cfg.B * cfg.hv * (cfg.dv // 64)
+    rs.gdn_verify(g.d, *args)                            # the same arguments, valid
+    torch.cuda.synchronize()
+
+
+def test_empty_batch_and_all_null():
+    import linear_attention_recurrent_rs_amd as rs
+    cfg = REDUCED['c1'].with_(B=4, null_rows=4, steps=2)
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init)
+    for j in range(2):
+        acc, ins, pol, next_T = H.step_data(cfg, j)
+        outs, wps = g.step(acc, ins, pol, next_T)
+        assert torch.all(outs[0] == H.SENTINEL_OUT) and torch.all(wps[0] == H.SENTINEL_WP)
+    H.check_untouched(cfg, g, init)
+    d0 = rs.Dims(0, 1, 1, 1, 16, 16, 4, 1, rs.F32, rs.F32, 0)   # empty batch: a no-op
+    assert rs._lib().rs_gdn_verify(rs.ctypes.byref(d0), *([None] * 14), None) == 0

@@ -1,0 +1,80 @@
+"""CPU tests of the C ABI library: it loads, exports every entry point include/rs.h
+declares, and validates arguments on the host (no GPU needed: validation precedes any
+device work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_recurrent_rs_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, 'include', 'rs.h')).read()
+    return sorted(set(re.findall(r'^\s*(?:rs_status|const char\*)\s+(rs_\w+)\s*\(', text, re.M)))
+
+
+def test_library_built():
+    assert os.path.exists(rs.library_path), 'run python -m linear_attention_recurrent_rs_amd.build'
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {'rs_gdn_verify', 'rs_kda_verify', 'rs_cursor_advance', 'rs_commit_fold',
+            'rs_materialize', 'rs_status_str'} <= set(names)
+    lib = ctypes.CDLL(rs.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = rs._lib()
+    for code in range(6):
+        assert lib.rs_status_str(code).decode().startswith('RS_')
+
+
+def _dims(**kw):
+    d = dict(batch=4, T=1, hk=2, hv=4, dk=128, dv=128, ring_cap=16, num_slots=8,
+             act_dtype=rs.BF16, state_dtype=rs.F32, tile_v=0)
+    d.update(kw)
+    return rs.Dims(*[d[f] for f, _ in rs.Dims._fields_])
+
+
+@pytest.mark.parametrize('kw,code', [
+    (dict(T=0), 2), (dict(T=17), 2), (dict(hv=3), 2), (dict(dk=24), 2), (dict(dk=272), 2),
+    (dict(dv=40), 2), (dict(act_dtype=7), 3), (dict(ring_cap=0), 2), (dict(T=4, ring_cap=3), 4),
+    (dict(tile_v=48), 2), (dict(tile_v=128, dv=64), 2), (dict(num_slots=0), 2),
+])
+def test_verify_validation(kw, code):
+    lib = rs._lib()
+    d = _dims(**kw)
+    assert lib.rs_gdn_verify(ctypes.byref(d), *([None] * 14), None) == code
+
+
+def test_verify_nullptr_and_kda_shape():
+    lib = rs._lib()
+    d = _dims()
+    assert lib.rs_gdn_verify(ctypes.byref(d), *([None] * 14), None) == 1
+    assert lib.rs_kda_verify(ctypes.byref(d), *([None] * 14), None) == 2   # hv != hk
+    assert lib.rs_gdn_verify(None, *([None] * 14), None) == 1
+
+
+def test_launch_info():
+    tv, wg, lds = rs.verify_launch_info(_dims(batch=64, hk=16, hv=32))
+    assert tv == 64 and wg == 64 * 32 * 2 and 0 < lds <= 160 * 1024
+    tv, wg, lds = rs.verify_launch_info(_dims(batch=64, hk=16, hv=32, tile_v=128))
+    assert tv == 128 and wg == 64 * 32
+
+
+def test_advance_and_fold_validation():
+    lib = rs._lib()
+    d = _dims()
+    assert lib.rs_cursor_advance(ctypes.byref(d), None, None, None, None, 0, 0, None, None) == 1
+    assert lib.rs_cursor_advance(ctypes.byref(d), None, None, None, None, 9, 0, None, None) == 2
+    assert lib.rs_cursor_advance(ctypes.byref(d), None, None, None, None, 2, 0, None, None) == 2
+    assert lib.rs_commit_fold(ctypes.byref(d), 0, *([None] * 6), None) == 1
+    assert lib.rs_commit_fold(ctypes.byref(d), 1, *([None] * 6), None) == 2
+    assert lib.rs_materialize(ctypes.byref(d), 0, *([None] * 7), None) == 1
