@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark: ReplaySSM GDN decode verify on one MI355X.
+
+Workload (GDN standard decode, Qwen3.5-shaped layers): batch 64 request rows of which 4
+are null (state slot -1), 16 key heads shared by 32 value heads, dk = dv = 128, fp32
+state, bf16 q/k/v/beta/gate, fp32 delta history, ring capacity 16, T = 1 (the metric's
+T = 3 case is reported alongside).  Cursors start staggered (row r at r mod 16, ring
+prefilled), so every launch mixes rows replaying 0..15 history records with rows that
+overflow and fold in-kernel, as a steady decode does.
+
+One step = one decode step of an 8-layer stack: a verify on each of 8 layer pools (each
+pool has its own state, ring and inputs; together > 1 GiB, so the 256 MB Infinity Cache
+cannot serve the state from one use to the next) and one advance of the shared cursor.
+Inputs are synthetic (seeded, from ``workloads``) and resident in HBM before timing.
+
+value = verified tokens per second per layer = live rows * T * layers / step time.
+roofline: the verify kernel; achieved = algorithmic bytes per launch (from the integer
+cursor model: state read, inputs, history records read, outputs and ring writes, the
+state write of rows that fold) / mean launch time from HIP events on the launch stream
+around every verify of the timed steps.  cpu_baseline: the fp64 oracle on a bounded
+sample of the same workload, single-threaded.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+
+
+def verify_bytes(cfg, n_list, fold_list):
+    """Algorithmic bytes of one verify launch: per live row, the state tile read once,
+    the window inputs, n history records, outputs and ring writes, and one state write
+    when the row folds in-kernel; plus its slot index and cursor."""
+    a = 2 if cfg.act_dtype == 'bf16' else 4
+    s = 2 if cfg.state_dtype == 'bf16' else 4
+    g_in = cfg.hv * cfg.dk * a if cfg.kda else cfg.hv * a
+    g_ring = cfg.hv * cfg.dk * 4 if cfg.kda else cfg.hv * 4
+    S_bytes = cfg.hv * cfg.dk * cfg.dv * s
+    inputs = cfg.T * (2 * cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * a + cfg.hv * a + g_in)
+    record = cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * 4 + g_ring
+    writes = cfg.T * (cfg.hv * cfg.dv * 4 + cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * 4 + g_ring)
+    total = 0
+    for n, f in zip(n_list, fold_list):
+        total += S_bytes + inputs + n * record + writes + (S_bytes if f else 0) + 8
+    return total
+
+
+def advance_model(cursor, slots, acc, T, L):
+    """The cursor advance of the fused-fold policy on the host, for byte accounting."""
+    for r, s in enumerate(slots):
+        if s < 0:
+            continue
+        n = int(cursor[s])
+        base = 0 if n + T > L else n
+        cursor[s] = base + int(acc[r])
+
+
+def run_gpu(T: int, steps: int, warmup: int, layers: int, tile_v: int, n_inputs: int = 4):
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+
+    cfg = W.CONFIGS['c1'].with_(T=T, layers=layers,
+                                accept=('const', 1) if T == 1 else ('uniform', 1, T))
+    dev = torch.device('cuda:0')
+    slots_np = W.slot_map(cfg)
+    cursor_np = W.initial_cursor(cfg, slots_np)
+
+    def to_dev(x, dt):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(dt).contiguous()
+
+    bf, f32 = torch.bfloat16, torch.float32
+    S, RK, RD, RG = [], [], [], []
+    for l in range(layers):
+        S.append(to_dev(W.initial_state(cfg, l), f32))
+        rk, rd, rg = W.initial_ring(cfg, cursor_np, l, fill=0.0)
+        RK.append(to_dev(rk, bf)); RD.append(to_dev(rd, f32)); RG.append(to_dev(rg, f32))
+    slots = torch.from_numpy(slots_np.astype(np.int32)).to(dev)
+    cursor = torch.from_numpy(cursor_np.astype(np.int32)).to(dev)
+    fold_len = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
+    counter = torch.zeros(cfg.B * cfg.hk, dtype=torch.int32, device=dev)
+    out = torch.empty(cfg.B * T, cfg.hv, cfg.dv, dtype=f32, device=dev)
+    d = rs.Dims(cfg.B, T, cfg.hk, cfg.hv, cfg.dk, cfg.dv, cfg.L, cfg.num_slots, rs.BF16, rs.F32,
+                tile_v)
+    BT = cfg.B * T
+    inputs, accepts, verify_calls, advance_calls = [], [], [], []
+    for j in range(n_inputs):
+        acc = W.accept_lengths(cfg, j)
+        accepts.append(acc)
+        acc_d = torch.from_numpy(acc.astype(np.int32)).to(dev)
+        per_layer = []
+        for l in range(layers):
+            inp = W.step_inputs(cfg, j, l)
+            t = (to_dev(inp.q.reshape(BT, cfg.hk, cfg.dk), bf), to_dev(inp.k.reshape(BT, cfg.hk, cfg.dk), bf),
+                 to_dev(inp.v.reshape(BT, cfg.hv, cfg.dv), bf), to_dev(inp.beta.reshape(BT, cfg.hv), bf),
+                 to_dev(inp.gate.reshape(BT, cfg.hv), bf))
+            inputs.append(t)
+            per_layer.append(rs.prepare_verify(False, d, *t, S[l], RK[l], RD[l], RG[l], cursor,
+                                               slots, out, None, counter))
+        verify_calls.append(per_layer)
+        advance_calls.append(rs.prepare_cursor_advance(d, cursor, fold_len, slots, acc_d,
+                                                       rs.FOLD_NONE, T))
+    tile, workgroups, lds = rs.verify_launch_info(d)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    host_cursor = cursor_np.copy()
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+
+    def step(s, events=None):
+        j = s % n_inputs
+        for l in range(layers):
+            if events is not None:
+                events[l][0].record(stream)
+            verify_calls[j][l](stream)
+            if events is not None:
+                events[l][1].record(stream)
+        advance_calls[j](stream)
+
+    for s in range(warmup):
+        step(s)
+        advance_model(host_cursor, slots_np, accepts[s % n_inputs], T, cfg.L)
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
+          for _ in range(steps)]
+    bytes_per_launch = []
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(warmup + s, ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(steps):
+        n = [int(host_cursor[slots_np[r]]) for r in live]
+        folds = [x + T > cfg.L for x in n]
+        bytes_per_launch.append(verify_bytes(cfg, n, folds))
+        advance_model(host_cursor, slots_np, accepts[(warmup + s) % n_inputs], T, cfg.L)
+    # the device cursors must follow the host model exactly
+    assert np.array_equal(cursor.cpu().numpy(), host_cursor), 'cursor model diverged'
+    durs = np.array([[ev[s][l][0].elapsed_time(ev[s][l][1]) for l in range(layers)]
+                     for s in range(steps)])            # ms
+    ms_step = (t1 - t0) * 1e3 / steps
+    mean_launch_ms = float(durs.mean())
+    mean_bytes = float(np.mean(bytes_per_launch))
+    achieved = mean_bytes / (mean_launch_ms * 1e-3) / 1e9
+    live_rows = len(live)
+    return {
+        'cfg': cfg, 'ms_per_step': ms_step,
+        'value': live_rows * T * layers / (ms_step * 1e-3),
+        'kernel_us': mean_launch_ms * 1e3, 'kernel_us_median': float(np.median(durs)) * 1e3,
+        'bytes_per_launch': mean_bytes, 'achieved_gbs': achieved,
+        'tokens_per_s_kernel': live_rows * T / (mean_launch_ms * 1e-3),
+        'tile_v': tile, 'workgroups': workgroups, 'lds_bytes': lds, 'live_rows': live_rows,
+    }
+
+
+def traffic_from_profiles(T):
+    """HBM bytes per verify launch from the committed counter summary, if one exists for
+    this workload (FETCH_SIZE + WRITE_SIZE per dispatch, calibrated on a copy kernel)."""
+    path = os.path.join(ROOT, 'profiles', 'gdn_verify_decode_b64_counters.md')
+    if not os.path.exists(path):
+        return None
+    m = re.search(rf'^traffic_bytes_per_launch T={T}: ([0-9.eE+]+)', open(path).read(), re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(T: int, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same decode workload:
+    8 live rows (all 32 value heads, full dk = dv = 128), one layer, consecutive steps
+    until the time budget is spent.  BLAS limited to one thread; the oracle's loops
+    and einsums run in one thread."""
+    from threadpoolctl import threadpool_limits
+    import workloads as W
+    from oracle import replay as rp
+
+    cfg = W.CONFIGS['c1'].with_(T=T, accept=('const', 1) if T == 1 else ('uniform', 1, T))
+    slots = W.slot_map(cfg)
+    cursor = W.initial_cursor(cfg, slots)
+    rows = [r for r in range(cfg.B) if slots[r] >= 0][:8]
+    rk, rd, rg = W.initial_ring(cfg, cursor, 0)
+    layer = rp.ReplayLayer(W.initial_state(cfg, 0), rk, rd, rg, False, cfg.G, cfg.L,
+                           slots=[slots[r] for r in rows])
+    fl = np.zeros(cfg.num_slots, np.int32)
+    steps, tokens, elapsed = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while elapsed < budget_s:
+            inp = W.step_inputs(cfg, steps, 0)          # input generation is not timed
+            acc = W.accept_lengths(cfg, steps)
+            sub = np.full(cfg.B, -1, np.int32)
+            sub[rows] = slots[rows]
+            ts = time.perf_counter()
+            rp.verify(layer, cursor, slots, inp, rows=rows)
+            rp.cursor_advance(cursor, fl, sub, acc, T, cfg.L, rp.FOLD_NONE)
+            elapsed += time.perf_counter() - ts
+            tokens += len(rows) * T
+            steps += 1
+    return {'value': tokens / elapsed, 'unit': 'verified tokens/s per layer', 'cores': 1,
+            'kind': 'oracle',
+            'sample': f'{len(rows)} live rows x 32 value heads (dk=dv=128, ring 16, T={T}), '
+                      f'{steps} decode steps of one layer, {elapsed:.1f} s, fp64 numpy'}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
+    ap.add_argument('--gpus', type=int, default=1)
+    ap.add_argument('--steps', type=int, default=50)
+    ap.add_argument('--warmup', type=int, default=10)
+    ap.add_argument('--layers', type=int, default=8, help='layer pools per step (rotating)')
+    ap.add_argument('--tile-v', type=int, default=0)
+    ap.add_argument('--only-T', type=int, default=0, help='run one window width only')
+    ap.add_argument('--no-cpu-baseline', action='store_true')
+    args = ap.parse_args()
+    world = int(os.environ.get('WORLD_SIZE', '1'))
+    if args.gpus != 1 or world != 1:
+        print(f'bench.py runs on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) is not '
+              'supported: the decode/verify path shards by request or by key-head group with '
+              'no exchange inside it, so one GPU shows the per-GPU kernel.', file=sys.stderr)
+        sys.exit(2)
+
+    Ts = [args.only_T] if args.only_T else [1, 3]
+    res = {}
+    for T in Ts:
+        res[T] = run_gpu(T, args.steps, args.warmup, args.layers, args.tile_v)
+        r = res[T]
+        print(f'# T={T}: {r["ms_per_step"]:.4f} ms/step, verify {r["kernel_us"]:.2f} us '
+              f'(median {r["kernel_us_median"]:.2f}), {r["achieved_gbs"]:.0f} GB/s, '
+              f'{r["value"] / 1e6:.3f} M tok/s/layer', file=sys.stderr, flush=True)
+    p = res[Ts[0]]
+    cfg = p['cfg']
+    traffic = traffic_from_profiles(Ts[0])
+    line = {
+        'metric': 'verified tokens/s per layer (GDN decode verify, batch 64, T=%d)' % Ts[0],
+        'value': round(p['value'], 1),
+        'unit': 'tokens/s',
+        'n_gpus': 1,
+        'steps': args.steps,
+        'warmup': args.warmup,
+        'ms_per_step': round(p['ms_per_step'], 5),
+        'higher_is_better': True,
+        'scaling': 'weak',
+        'vs_baseline': None,
+        'dtype': 'f32',
+        'data': 'synthetic',
+        'config': {'workload': 'gdn_decode_qwen35_shaped_b64', 'batch': cfg.B,
+                   'live_rows': p['live_rows'], 'hk': cfg.hk, 'hv': cfg.hv, 'dk': cfg.dk,
+                   'dv': cfg.dv, 'ring': cfg.L, 'T': cfg.T, 'state': 'f32', 'inputs': 'bf16',
+                   'layers_per_step': args.layers, 'tile_v': p['tile_v']},
+        'roofline': {'bound': 'hbm', 'achieved': round(p['achieved_gbs'], 1),
+                     'peak': HBM_PEAK_GBS, 'unit': 'GB/s',
+                     'frac': round(p['achieved_gbs'] / HBM_PEAK_GBS, 4),
+                     'traffic': traffic, 'kernel': 'rs::verify_kernel',
+                     'kernel_us': round(p['kernel_us'], 3),
+                     'bytes_per_launch': int(p['bytes_per_launch'])},
+    }
+    extra = {}
+    for T in Ts[1:]:
+        r = res[T]
+        extra[f'T{T}'] = {'value': round(r['value'], 1), 'ms_per_step': round(r['ms_per_step'], 5),
+                          'kernel_us': round(r['kernel_us'], 3),
+                          'achieved_gbs': round(r['achieved_gbs'], 1),
+                          'frac': round(r['achieved_gbs'] / HBM_PEAK_GBS, 4),
+                          'bytes_per_launch': int(r['bytes_per_launch'])}
+    if extra:
+        line['extra'] = extra
+    if not args.no_cpu_baseline:
+        line['cpu_baseline'] = cpu_baseline(Ts[0])
+        cb = line['cpu_baseline']
+        cb['value'] = round(cb['value'], 2)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == '__main__':
+    main()

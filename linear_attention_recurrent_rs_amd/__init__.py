@@ -18,6 +18,7 @@ import torch
 
 __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'commit_fold',
            'materialize', 'verify_launch_info', 'library_path', 'F32', 'BF16',
+           'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
            'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE']
 
 F32, BF16 = 0, 1
@@ -102,8 +103,8 @@ def _check(status: int, where: str):
         raise RSError(status, where)
 
 
-def _verify(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
-            slot_idx, out, write_pos_out, group_counter, stream):
+def _verify_ptrs(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                 slot_idx, out, write_pos_out, group_counter):
     at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
     BT, S, L = d.batch * d.T, d.num_slots, d.ring_cap
     g_per = d.hv * d.dk if kda else d.hv
@@ -120,6 +121,13 @@ def _verify(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring
         _ptr(write_pos_out, 'write_pos_out', d.batch, torch.int32, optional=True),
         _ptr(group_counter, 'group_counter', d.batch * d.hk, torch.int32),
     ]
+    return args
+
+
+def _verify(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+            slot_idx, out, write_pos_out, group_counter, stream):
+    args = _verify_ptrs(kda, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                        slot_idx, out, write_pos_out, group_counter)
     fn = _lib().rs_kda_verify if kda else _lib().rs_gdn_verify
     _check(fn(ctypes.byref(d), *args, _stream(stream)), 'rs_kda_verify' if kda else 'rs_gdn_verify')
 
@@ -189,3 +197,57 @@ def verify_launch_info(d: Dims, kda: bool = False):
                                         ctypes.byref(wg), ctypes.byref(lds)),
            'rs_verify_launch_info')
     return tv.value, wg.value, lds.value
+
+
+# ----------------------------------------------------------------------------- prepared calls
+# For launch loops: the tensors are checked and their pointers marshalled once; each call
+# of the returned function is then a single C call on the given stream.  The returned
+# function holds references to its tensors, so their memory stays allocated while it lives.
+
+def prepare_verify(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                   cursor, slot_idx, out, write_pos_out=None, group_counter=None):
+    args = _verify_ptrs(kda, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                        slot_idx, out, write_pos_out, group_counter)
+    fn = _lib().rs_kda_verify if kda else _lib().rs_gdn_verify
+    dref = ctypes.byref(d)
+    name = 'rs_kda_verify' if kda else 'rs_gdn_verify'
+
+    def call(stream=None):
+        st = fn(dref, *args, _stream(stream))
+        if st:
+            raise RSError(st, name)
+    call.dims = d
+    call.tensors = (q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx, out,
+                    write_pos_out, group_counter)
+    return call
+
+
+def prepare_cursor_advance(d: Dims, cursor, fold_len, slot_idx, accept_len,
+                           policy: int = FOLD_NONE, next_T: int = 0, force_mask=None):
+    args = [_ptr(cursor, 'cursor', d.num_slots, torch.int32),
+            _ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    fm = _ptr(force_mask, 'force_mask', d.batch, torch.uint8, optional=True)
+    fn, dref = _lib().rs_cursor_advance, ctypes.byref(d)
+
+    def call(stream=None):
+        st = fn(dref, *args, int(policy), int(next_T), fm, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_cursor_advance')
+    call.tensors = (cursor, fold_len, slot_idx, accept_len, force_mask)
+    return call
+
+
+def prepare_commit_fold(d: Dims, kda: bool, state, ring_k, ring_d, ring_g, fold_len, slot_idx):
+    p = _fold_ptrs(d, kda, state, ring_k, ring_d, ring_g)
+    rest = [_ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32)]
+    fn, dref = _lib().rs_commit_fold, ctypes.byref(d)
+
+    def call(stream=None):
+        st = fn(dref, int(kda), *p, *rest, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_commit_fold')
+    call.tensors = (state, ring_k, ring_d, ring_g, fold_len, slot_idx)
+    return call

@@ -40,18 +40,35 @@ int choose_bv(const rs_dims* d) {
   return 16;
 }
 
-rs_status verify_plan(const rs_dims* d, bool kda, int* bv, int* tmax, rs::LdsLayout* lay) {
+// The dk = 128 / bf16-input verify (rs_verify_fast.hip) covers the tile widths 32, 64
+// and 128; every other shape takes the general verify (rs_kernels.hip).
+bool use_fast(const rs_dims* d, int bv) {
+  return d->dk == 128 && d->act_dtype == RS_BF16 && (bv == 32 || bv == 64 || bv == 128);
+}
+
+struct VerifyPlan {
+  int bv = 0, tmax = 0;
+  bool fast = false;
+  rs::LdsLayout lay{};
+  rs::FastLayout flay{};
+  int lds() const { return fast ? flay.total : lay.total; }
+};
+
+rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
   rs_status st = check_common(d, true);
   if (st != RS_OK) return st;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
-  *tmax = tmax_of(d->T);
-  *bv = choose_bv(d);
-  *lay = rs::verify_layout(kda, dbytes(d->state_dtype), *bv, *tmax, d->T, d->dk, d->ring_cap);
-  while (lay->total > kMaxLds && d->tile_v == 0 && *bv > 16) {
-    *bv /= 2;
-    *lay = rs::verify_layout(kda, dbytes(d->state_dtype), *bv, *tmax, d->T, d->dk, d->ring_cap);
+  p->tmax = tmax_of(d->T);
+  p->bv = choose_bv(d);
+  for (;;) {
+    p->fast = use_fast(d, p->bv);
+    if (p->fast) p->flay = rs::fast_layout(kda, p->bv, p->tmax, d->T, d->ring_cap);
+    else p->lay = rs::verify_layout(kda, dbytes(d->state_dtype), p->bv, p->tmax, d->T, d->dk,
+                                    d->ring_cap);
+    if (p->lds() <= kMaxLds || d->tile_v != 0 || p->bv <= 16) break;
+    p->bv /= 2;
   }
-  if (lay->total > kMaxLds) return RS_E_SHAPE;
+  if (p->lds() > kMaxLds) return RS_E_SHAPE;
   return RS_OK;
 }
 
@@ -60,14 +77,14 @@ rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, 
                       float* ring_d, float* ring_g, const int32_t* cursor,
                       const int32_t* slot_idx, float* out, int32_t* write_pos_out,
                       int32_t* group_counter, hipStream_t stream) {
-  int bv = 0, tmax = 0;
-  rs::LdsLayout lay{};
-  rs_status st = verify_plan(d, kda, &bv, &tmax, &lay);
+  VerifyPlan plan;
+  rs_status st = verify_plan(d, kda, &plan);
   if (st != RS_OK) return st;
   if (d->batch == 0) return RS_OK;
   if (!q || !k || !v || !beta || !gate || !state || !ring_k || !ring_d || !ring_g || !cursor ||
       !slot_idx || !out || !group_counter)
     return RS_E_NULLPTR;
+  const int bv = plan.bv;
   rs::VerifyArgs a{};
   a.B = d->batch; a.T = d->T; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
   a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
@@ -75,9 +92,11 @@ rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, 
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate;
   a.state = state; a.ring_k = ring_k; a.ring_d = ring_d; a.ring_g = ring_g;
   a.cursor = cursor; a.slot_idx = slot_idx; a.out = out; a.write_pos_out = write_pos_out;
-  a.group_counter = group_counter; a.lay = lay;
-  hipError_t e = rs::launch_verify(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv,
-                                   tmax, a, stream);
+  a.group_counter = group_counter; a.lay = plan.lay;
+  hipError_t e = plan.fast
+      ? rs::launch_verify_fast(kda, d->state_dtype == RS_BF16, bv, plan.tmax, a, plan.flay, stream)
+      : rs::launch_verify(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv, plan.tmax,
+                          a, stream);
   return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
 }
 
@@ -182,13 +201,12 @@ const char* rs_status_str(rs_status s) {
 
 rs_status rs_verify_launch_info(const rs_dims* dims, int is_kda, int32_t* tile_v,
                                 int32_t* workgroups, int32_t* lds_bytes) {
-  int bv = 0, tmax = 0;
-  rs::LdsLayout lay{};
-  rs_status st = verify_plan(dims, is_kda != 0, &bv, &tmax, &lay);
+  VerifyPlan plan;
+  rs_status st = verify_plan(dims, is_kda != 0, &plan);
   if (st != RS_OK) return st;
-  if (tile_v) *tile_v = bv;
-  if (workgroups) *workgroups = dims->batch * dims->hv * (dims->dv / bv);
-  if (lds_bytes) *lds_bytes = lay.total;
+  if (tile_v) *tile_v = plan.bv;
+  if (workgroups) *workgroups = dims->batch * dims->hv * (dims->dv / plan.bv);
+  if (lds_bytes) *lds_bytes = plan.lds();
   return RS_OK;
 }
 

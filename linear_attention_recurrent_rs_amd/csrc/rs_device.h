@@ -105,7 +105,69 @@ __device__ __forceinline__ void load_lds_16(const void* g, void* lds_wave_base) 
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
                                    16, 0, 0);
 }
+// Same, 4 bytes per lane: lane l writes lds_wave_base + 4*l.
+__device__ __forceinline__ void load_lds_4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   4, 0, 0);
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector-memory operations
+// of this wave are outstanding and leaves the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic that waits for this wave's LDS operations and for all
+// but its last N vector-memory operations, and no more: unlike __syncthreads(), loads
+// still in flight (a state tile streaming into registers) stay in flight.  Writes that
+// reach LDS through HBM->LDS copies count as vector-memory operations.  The memory
+// clobbers keep the compiler from moving LDS accesses across the barrier.
+template <int N = 63>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Keep the compiler from moving memory operations or scheduling instructions across.
+__device__ __forceinline__ void code_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Asynchronous copy of nrows rows of row_bytes (a multiple of 16) from global memory (row r
+// at g + r * gstride bytes) into LDS, rows packed back to back at dst.  All threads of the
+// workgroup take part; wait_vmem*() + a barrier before reading dst.
+__device__ __forceinline__ void dma_rows(const void* g, size_t gstride, int row_bytes,
+                                         int nrows, void* dst) {
+  const int cpr = row_bytes >> 4, n = nrows * cpr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* gb = static_cast<const char*>(g);
+  char* db = static_cast<char*>(dst);
+  for (int p0 = wave * 64; p0 < n; p0 += kThreads) {
+    const int p = p0 + lane;
+    if (p < n) {
+      const int r = p / cpr, c = p - r * cpr;
+      load_lds_16(gb + (size_t)r * gstride + c * 16, db + p0 * 16);
+    }
+  }
+}
+
+// Asynchronous gather of n 4-byte words (word i at g + i * gstride bytes) into LDS dst[i].
+__device__ __forceinline__ void dma_words(const void* g, size_t gstride, int n, void* dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* gb = static_cast<const char*>(g);
+  char* db = static_cast<char*>(dst);
+  for (int p0 = wave * 64; p0 < n; p0 += kThreads) {
+    const int p = p0 + lane;
+    if (p < n) load_lds_4(gb + (size_t)p * gstride, db + p0 * 4);
+  }
+}
 
 }  // namespace rs

@@ -113,9 +113,65 @@ inline LdsLayout fold_layout(bool kda, int st_bytes, int bv, int dk, int L, bool
   return l;
 }
 
-// Launchers (defined in rs_kernels.hip).  Return hipGetLastError() after the launch.
+// LDS plan of the dk = 128, bf16-input verify (rs_verify_fast.hip).  Byte offsets.
+struct FastLayout {
+  int xkq;      // window q_t then k_t, bf16 [2T x 128]             (HBM -> LDS copy)
+  int xv;       // window v_t of this tile, bf16 [T x bv]           (HBM -> LDS copy)
+  int xg;       // KDA window gates, bf16 [T x 128]                 (HBM -> LDS copy)
+  int hkeys;    // history keys, bf16 [L x 128]                     (HBM -> LDS copy)
+  int hd;       // history deltas of this tile, fp32 [L x bv]       (HBM -> LDS copy)
+  int hg;       // history gates, fp32 [L] (GDN) or [L x 128] (KDA) (HBM -> LDS copy)
+  int khat;     // KDA: keys times their suffix decay, fp32 [L x xs_stride]
+  int gam_i;    // GDN: suffix decay of each record, fp32 [L]
+  int Gam;      // total history decay per key channel, fp32 [128]
+  int xs;       // window vectors times the in-window prefix decay [nvec_pad x xs_stride]
+  int xr;       // readout vectors: Gam (.) xs [nvec_pad x xs_stride]
+  int C;        // history scores khat_i . xs_m [L x 2*tmax]
+  int P;        // readout [2*tmax x bv]
+  int red;      // cross-wave reduction [4 x vpp x bv]
+  int Am, Qm;   // window pair scalars [tmax x tmax]
+  int bw, gw;   // betas, GDN gates [tmax]
+  int flags;
+  int total;
+  int xs_stride;
+  int nvec_pad;
+};
+
+inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
+  auto al = [](int x) { return (x + 15) & ~15; };
+  const int dk = 128, vpp = readout_vpp(tmax);
+  FastLayout l{};
+  int o = 0;
+  l.xs_stride = dk + 4;
+  l.nvec_pad = ((2 * T + vpp - 1) / vpp) * vpp;
+  l.xkq = o; o += al(2 * tmax * dk * 2);
+  l.xv = o; o += al(tmax * bv * 2);
+  l.xg = o; o += kda ? al(tmax * dk * 2) : 0;
+  l.hkeys = o; o += al(L * dk * 2);
+  l.hd = o; o += al(L * bv * 4);
+  l.hg = o; o += al(kda ? L * dk * 4 : L * 4);
+  l.khat = o; o += kda ? al(L * l.xs_stride * 4) : 0;
+  l.gam_i = o; o += al(L * 4);
+  l.Gam = o; o += al(dk * 4);
+  l.xs = o; o += al(l.nvec_pad * l.xs_stride * 4);
+  l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
+  l.C = o; o += al(L * 2 * tmax * 4);
+  l.P = o; o += al(2 * tmax * bv * 4);
+  l.red = o; o += al(4 * vpp * bv * 4);
+  l.Am = o; o += al(tmax * tmax * 4);
+  l.Qm = o; o += al(tmax * tmax * 4);
+  l.bw = o; o += al(tmax * 4);
+  l.gw = o; o += al(tmax * 4);
+  l.flags = o; o += 16;
+  l.total = o;
+  return l;
+}
+
+// Launchers (defined in rs_kernels.hip and rs_verify_fast.hip).  Return hipGetLastError() after the launch.
 hipError_t launch_verify(bool kda, int act_bf16, int state_bf16, int bv, int tmax,
                          const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_fast(bool kda, int state_bf16, int bv, int tmax, const VerifyArgs& a,
+                              const FastLayout& lay, hipStream_t s);
 hipError_t launch_fold(bool kda, int act_bf16, int state_bf16, int bv, bool materialize,
                        const FoldArgs& a, hipStream_t s);
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
