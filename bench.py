@@ -164,14 +164,48 @@ def run_gpu(T: int, steps: int, warmup: int, layers: int, tile_v: int, n_inputs:
     }
 
 
+KERNEL_SOURCES = ('rs_verify_fast.hip', 'rs_device.h', 'rs_internal.h')
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the fast verify kernel, so that counter readings taken
+    on an older kernel are not reported against a changed one."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, 'linear_attention_recurrent_rs_amd', 'csrc', name), 'rb') as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def traffic_from_profiles(T):
     """HBM bytes per verify launch from the committed counter summary, if one exists for
-    this workload (FETCH_SIZE + WRITE_SIZE per dispatch, calibrated on a copy kernel)."""
+    this workload and was taken on the current kernel sources (FETCH_SIZE + WRITE_SIZE per
+    dispatch, each calibrated on a plain copy); else None."""
     path = os.path.join(ROOT, 'profiles', 'gdn_verify_decode_b64_counters.md')
     if not os.path.exists(path):
         return None
-    m = re.search(rf'^traffic_bytes_per_launch T={T}: ([0-9.eE+]+)', open(path).read(), re.M)
+    text = open(path).read()
+    src = re.search(r'^kernel_source_sha256: ([0-9a-f]+)', text, re.M)
+    if not src or src.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf'^traffic_bytes_per_launch T={T}: ([0-9.eE+]+)', text, re.M)
     return float(m.group(1)) if m else None
+
+
+def copy_calibration(mib: int = 256, reps: int = 4):
+    """Plain device-to-device copies of a known size (mib MiB read + mib MiB written per
+    launch), run before the benchmark so that one hardware-counter pass sees both them and
+    the verify launches: the ratio of a counter's reading on the copy to the copy's true
+    bytes calibrates that counter."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device='cuda:0')
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f'# copy calibration: {reps} copies of {mib} MiB', file=sys.stderr, flush=True)
 
 
 def cpu_baseline(T: int, budget_s: float = 12.0):
@@ -219,7 +253,14 @@ def main():
     ap.add_argument('--tile-v', type=int, default=0)
     ap.add_argument('--only-T', type=int, default=0, help='run one window width only')
     ap.add_argument('--no-cpu-baseline', action='store_true')
+    ap.add_argument('--source-hash', action='store_true',
+                    help='print the hash of the verify kernel sources and exit')
+    ap.add_argument('--copy-calibration', action='store_true',
+                    help='first run plain copies of 256 MiB (for counter calibration)')
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     world = int(os.environ.get('WORLD_SIZE', '1'))
     if args.gpus != 1 or world != 1:
         print(f'bench.py runs on one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) is not '
@@ -227,6 +268,8 @@ def main():
               'no exchange inside it, so one GPU shows the per-GPU kernel.', file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
     Ts = [args.only_T] if args.only_T else [1, 3]
     res = {}
     for T in Ts:
@@ -258,7 +301,7 @@ def main():
         'roofline': {'bound': 'hbm', 'achieved': round(p['achieved_gbs'], 1),
                      'peak': HBM_PEAK_GBS, 'unit': 'GB/s',
                      'frac': round(p['achieved_gbs'] / HBM_PEAK_GBS, 4),
-                     'traffic': traffic, 'kernel': 'rs::verify_kernel',
+                     'traffic': traffic, 'kernel': 'rs::verify_fast_kernel',
                      'kernel_us': round(p['kernel_us'], 3),
                      'bytes_per_launch': int(p['bytes_per_launch'])},
     }
