@@ -11,6 +11,7 @@ constexpr int kWaves = 4;
 constexpr int kXcds = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint16_t bf16;
 
 // ------------------------------------------------------------------ number formats
@@ -53,6 +54,28 @@ __device__ __forceinline__ void store4(bf16* p, f4 v) {
   u.y = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
   *reinterpret_cast<uint2*>(p) = u;
 }
+// The same, with the non-temporal hint: data streamed once, kept out of the caches' way.
+__device__ __forceinline__ f4 load4_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+}
+__device__ __forceinline__ f4 load4_nt(const bf16* p) {
+  const u2 u = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+  f4 r;
+  r[0] = __uint_as_float(u[0] << 16);
+  r[1] = __uint_as_float(u[0] & 0xffff0000u);
+  r[2] = __uint_as_float(u[1] << 16);
+  r[3] = __uint_as_float(u[1] & 0xffff0000u);
+  return r;
+}
+__device__ __forceinline__ void store4_nt(float* p, f4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
+}
+__device__ __forceinline__ void store4_nt(bf16* p, f4 v) {
+  u2 u;
+  u[0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+  u[1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
+  __builtin_nontemporal_store(u, reinterpret_cast<u2*>(p));
+}
 template <typename T> __device__ __forceinline__ f4 round4(f4 v) {
   f4 r;
   r[0] = stored_value<T>(v[0]); r[1] = stored_value<T>(v[1]);
@@ -93,11 +116,30 @@ __device__ __forceinline__ int xcd_remap(int p, int n) {
   return xcd * per + (xcd < extra ? xcd : extra) + idx;
 }
 
+// Same, for work in groups of gs consecutive logical indices that share data (the tiles
+// of the value heads of one key group): whole groups go round-robin over the XCDs, so a
+// group shares one L2 and every XCD gets an even share of rows.  Needs n to be a multiple
+// of 8 * gs (else the contiguous mapping above).  Bijective on [0, n).
+__device__ __forceinline__ int xcd_group_remap(int p, int n, int gs) {
+  if (n % (kXcds * gs) != 0) return xcd_remap(p, n);
+  const int xcd = p % kXcds, q = p / kXcds;
+  return ((q / gs) * kXcds + xcd) * gs + q % gs;
+}
+
 // ------------------------------------------------------------------ MFMA
 // D(16x16) += A(16x4) B(4x16), fp32.  Lane l supplies A[l%16][l/16] and B[l/16][l%16];
 // it holds D[4*(l/16)+i][l%16] in element i of the accumulator.
 __device__ __forceinline__ f4 mfma_16x16x4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+typedef short s4 __attribute__((ext_vector_type(4)));
+// D(16x16) += A(16x16) B(16x16), bf16 operands (products exact in fp32), fp32 accumulate.
+// Lane l supplies four K entries of row l%16 of A and the same four K entries of column
+// l%16 of B; it holds D[4*(l/16)+i][l%16] in element i of the accumulator.  Which four K
+// entries a lane holds is immaterial as long as A and B agree.
+__device__ __forceinline__ f4 mfma_bf16_16x16x16(s4 a, s4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Direct HBM -> LDS copy of 16 bytes per lane: lane l writes lds_wave_base + 16*l.
@@ -157,6 +199,18 @@ __device__ __forceinline__ void dma_rows(const void* g, size_t gstride, int row_
       load_lds_16(gb + (size_t)r * gstride + c * 16, db + p0 * 16);
     }
   }
+}
+
+// Asynchronous copy of nrows rows of 256 bytes (row r at g + r * gstride bytes) into LDS
+// rows dst_stride bytes apart (a padded stride spreads equal columns of consecutive rows
+// over different banks).  One row per wave instruction, 16 lanes of 16 bytes.
+__device__ __forceinline__ void dma_rows_256(const void* g, size_t gstride, int nrows,
+                                             void* dst, int dst_stride) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* gb = static_cast<const char*>(g);
+  char* db = static_cast<char*>(dst);
+  for (int r = wave; r < nrows; r += kWaves)
+    if (lane < 16) load_lds_16(gb + (size_t)r * gstride + lane * 16, db + r * dst_stride);
 }
 
 // Asynchronous gather of n 4-byte words (word i at g + i * gstride bytes) into LDS dst[i].

@@ -114,6 +114,7 @@ inline LdsLayout fold_layout(bool kda, int st_bytes, int bv, int dk, int L, bool
 }
 
 // LDS plan of the dk = 128, bf16-input verify (rs_verify_fast.hip).  Byte offsets.
+// Rows of 128 bf16 (keys, queries, KDA gates) sit kKeyStride elements apart.
 struct FastLayout {
   int xkq;      // window q_t then k_t, bf16 [2T x 128]             (HBM -> LDS copy)
   int xv;       // window v_t of this tile, bf16 [T x bv]           (HBM -> LDS copy)
@@ -121,48 +122,47 @@ struct FastLayout {
   int hkeys;    // history keys, bf16 [L x 128]                     (HBM -> LDS copy)
   int hd;       // history deltas of this tile, fp32 [L x bv]       (HBM -> LDS copy)
   int hg;       // history gates, fp32 [L] (GDN) or [L x 128] (KDA) (HBM -> LDS copy)
+  int gam_i;    // GDN: suffix decay of each history record, fp32 [L]
   int khat;     // KDA: keys times their suffix decay, fp32 [L x xs_stride]
-  int gam_i;    // GDN: suffix decay of each record, fp32 [L]
-  int Gam;      // total history decay per key channel, fp32 [128]
-  int xs;       // window vectors times the in-window prefix decay [nvec_pad x xs_stride]
-  int xr;       // readout vectors: Gam (.) xs [nvec_pad x xs_stride]
-  int C;        // history scores khat_i . xs_m [L x 2*tmax]
-  int P;        // readout [2*tmax x bv]
-  int red;      // cross-wave reduction [4 x vpp x bv]
+  int Gam;      // KDA: total history decay per key channel, fp32 [128]
+  int xs;       // KDA: window vectors times the in-window prefix decay [2*tmax x xs_stride]
+  int xr;       // readout vectors, q_t and k_t interleaved [nvec_pad x xs_stride]
+  int C;        // history scores [lp x cs] (GDN: undecayed) or 4 partial sums of them (KDA)
+  int red;      // per-wave readout partial sums [4 x nvec_pad x bv]
   int Am, Qm;   // window pair scalars [tmax x tmax]
-  int bw, gw;   // betas, GDN gates [tmax]
-  int flags;
   int total;
   int xs_stride;
   int nvec_pad;
+  int cs;       // row stride of C: 2*tmax rounded up to 16
+  int lp;       // rows of C: L rounded up to 16
 };
+
+constexpr int kKeyStride = 136;   // 128 bf16 + 16 bytes of padding
 
 inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
   auto al = [](int x) { return (x + 15) & ~15; };
-  const int dk = 128, vpp = readout_vpp(tmax);
+  const int dk = 128, vpp = readout_vpp(tmax), ks = kKeyStride;
   FastLayout l{};
   int o = 0;
   l.xs_stride = dk + 4;
   l.nvec_pad = ((2 * T + vpp - 1) / vpp) * vpp;
-  l.xkq = o; o += al(2 * tmax * dk * 2);
+  l.cs = (2 * tmax + 15) & ~15;
+  l.lp = (L + 15) & ~15;
+  l.xkq = o; o += al(2 * tmax * ks * 2);
   l.xv = o; o += al(tmax * bv * 2);
-  l.xg = o; o += kda ? al(tmax * dk * 2) : 0;
-  l.hkeys = o; o += al(L * dk * 2);
+  l.xg = o; o += kda ? al(tmax * ks * 2) : 0;
+  l.hkeys = o; o += al(L * ks * 2);
   l.hd = o; o += al(L * bv * 4);
   l.hg = o; o += al(kda ? L * dk * 4 : L * 4);
+  l.gam_i = o; o += kda ? 0 : al(L * 4);
   l.khat = o; o += kda ? al(L * l.xs_stride * 4) : 0;
-  l.gam_i = o; o += al(L * 4);
-  l.Gam = o; o += al(dk * 4);
-  l.xs = o; o += al(l.nvec_pad * l.xs_stride * 4);
+  l.Gam = o; o += kda ? al(dk * 4) : 0;
+  l.xs = o; o += kda ? al(2 * tmax * l.xs_stride * 4) : 0;
   l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
-  l.C = o; o += al(L * 2 * tmax * 4);
-  l.P = o; o += al(2 * tmax * bv * 4);
-  l.red = o; o += al(4 * vpp * bv * 4);
+  l.C = o; o += al((kda ? 4 : 1) * l.lp * l.cs * 4);
+  l.red = o; o += al(4 * l.nvec_pad * bv * 4);
   l.Am = o; o += al(tmax * tmax * 4);
   l.Qm = o; o += al(tmax * tmax * 4);
-  l.bw = o; o += al(tmax * 4);
-  l.gw = o; o += al(tmax * 4);
-  l.flags = o; o += 16;
   l.total = o;
   return l;
 }

@@ -2,19 +2,30 @@
 //
 // Same method as verify_kernel in rs_kernels.hip; the difference is how the workgroup
 // spends its time.  The [128 x BV] state tile is the only large operand, and it streams
-// straight into registers (four rows x four columns per thread, 256-byte row segments per
-// 16 lanes) as one compile-time block of loads, issued after every small operand has
-// been queued by direct HBM->LDS copies.  One explicit wait for "all but the tile" then
-// lets the scalar work (decays, window pair products, history scores) run while the
-// tile is still in flight.
+// (non-temporal loads: read once, no reuse) straight into registers (four rows x four columns per thread, 256-byte row segments per
+// 16 lanes) as one block of loads, issued after every small operand has been queued by
+// direct HBM->LDS copies.  One explicit wait for "all but the tile" then lets everything
+// that does not need the state run while the tile is still in flight, and that part is
+// kept short: a workgroup holds its slot on the CU until its last instruction, and every
+// cycle it spends after its tile has landed is a cycle in which the slot moves no bytes.
+//
+//  * Window and history scores are small dense contractions over dk: one 16 x 16 MFMA
+//    tile covers up to 16 score rows (history records, then window keys) against up to 16
+//    window vectors (q_0.., k_0..).  GDN feeds the bf16 inputs to bf16 MFMAs (products
+//    are exact in fp32) and applies the scalar decays to the results; KDA's decays are
+//    per channel, so its history keys are scaled first and go through fp32 MFMAs, each
+//    wave taking a quarter of dk.
+//  * The history part of the readout, sum_i d_i (khat_i . x), is summed into registers
+//    before the tile is touched.
 //
 // History is not replayed into the tile.  With H = Gam (.) S + sum_i khat_i d_i^T
 // (khat_i = gamma_i (.) k_i), the readout splits into
 //   H^T x = S^T (Gam (.) x) + sum_i d_i (khat_i . x),
-// a pass over the registers plus nh scores per window vector (sglang commit 5: history
-// terms only when write_pos is nonzero).  A row whose window would overflow the ring
-// instead folds its prefix into the registers, writes the state back once and reads
-// out with no history.
+// a pass over the registers plus nh scores per window vector (the history terms only
+// when write_pos is nonzero).  A row whose window would overflow the ring instead folds
+// its prefix into the registers, writes the state back once and reads out with no
+// history.  Every sum over window positions runs over causal positions only, so values at
+// rejected positions never reach accepted outputs.
 #include "rs_device.h"
 #include "rs_internal.h"
 
@@ -31,18 +42,43 @@ __device__ __forceinline__ float load_bf16_uniform(const bf16* p) {
 
 __device__ __forceinline__ f4 bf16x4(const bf16* p) { return load4(p); }
 
+// Product of the window gates held in registers over a lane-dependent range of window
+// positions, (lo, hi], by selection rather than register-array indexing.
+template <int TMAX>
+__device__ __forceinline__ float gate_product(const float (&g)[TMAX], int lo, int hi) {
+  float p = 1.f;
+#pragma unroll
+  for (int w = 0; w < TMAX; ++w)
+    if (w > lo && w <= hi) p *= g[w];
+  return p;
+}
+
+template <int TMAX>
+__device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < TMAX; ++w)
+    if (w == t) r = x[w];
+  return r;
+}
+
 template <bool KDA, typename ST, int BV, int TMAX>
 __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
-  constexpr int DK = 128;
-  constexpr int CC = BV / 4, RG = kThreads / CC, NQ = DK / 4, QPT = NQ / RG;
-  constexpr int VPP = (2 * TMAX < 8) ? 2 * TMAX : 8;
-  constexpr int CS = 2 * TMAX;                 // row stride of the score matrix
-  static_assert(NQ % RG == 0 && QPT >= 1, "tile split");
+  constexpr int DK = 128, KS = kKeyStride;
+  // Tile split: thread (rg, cc) holds rows 4*(rg + RG*j) + i (j < QPT, i < 4) of column
+  // quad cc, so that each load instruction of a wave covers whole 256-byte row segments
+  // (rows of a 64-column tile); the dk reduction of the readout then runs over the row
+  // groups within a wave (lane shuffles) and over the 4 waves (LDS).
+  constexpr int CC = BV / 4, RG = kThreads / CC, QPT = DK / (4 * RG);
+  constexpr int NV2 = 2 * TMAX;
+  constexpr int VPP = (NV2 < 8) ? NV2 : 8;           // readout vectors per pass
+  constexpr int NPASS = NV2 / VPP;
+  static_assert(QPT >= 1 && DK % (4 * RG) == 0 && CC <= 64, "tile split");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cc = tid % CC, rg = tid / CC;
-  const int lid = xcd_remap(blockIdx.x, a.nblocks);
+  const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
   const int vt = lid % a.NV;
   const int h = (lid / a.NV) % a.hv;
   const int row = lid / (a.NV * a.hv);
@@ -52,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   const int T = a.T, L = a.L, hv = a.hv, hk = a.hk, dv = a.dv;
   const int kh = h / a.G, col0 = vt * BV;
   const size_t tok0 = (size_t)row * T;
-  const int XS = lay.xs_stride;
+  const int XS = lay.xs_stride, CS = lay.cs;
 
   bf16* xkq = reinterpret_cast<bf16*>(smem + lay.xkq);
   bf16* xv = reinterpret_cast<bf16*>(smem + lay.xv);
@@ -60,19 +96,15 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
   float* hd = reinterpret_cast<float*>(smem + lay.hd);
   float* hg = reinterpret_cast<float*>(smem + lay.hg);
-  float* khat = reinterpret_cast<float*>(smem + lay.khat);
   float* gam_i = reinterpret_cast<float*>(smem + lay.gam_i);
-  float* Gam = reinterpret_cast<float*>(smem + lay.Gam);
+  float* khat = reinterpret_cast<float*>(smem + lay.khat);
+  float* Gamv = reinterpret_cast<float*>(smem + lay.Gam);
   float* xs = reinterpret_cast<float*>(smem + lay.xs);
   float* xr = reinterpret_cast<float*>(smem + lay.xr);
   float* Cs = reinterpret_cast<float*>(smem + lay.C);
-  float* P = reinterpret_cast<float*>(smem + lay.P);
   float* red = reinterpret_cast<float*>(smem + lay.red);
   float* Am = reinterpret_cast<float*>(smem + lay.Am);
   float* Qm = reinterpret_cast<float*>(smem + lay.Qm);
-  float* bw = reinterpret_cast<float*>(smem + lay.bw);
-  float* gw = reinterpret_cast<float*>(smem + lay.gw);
-  int* flags = reinterpret_cast<int*>(smem + lay.flags);
 
   const bf16* qg = static_cast<const bf16*>(a.q);
   const bf16* kg = static_cast<const bf16*>(a.k);
@@ -88,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   const bool fold = n + T > L;                           // the window would overflow
   const int base = fold ? 0 : n;                         // write_pos
   const int nh = n;
-  float beta_s[TMAX], gate_s[TMAX];
+  float beta_s[TMAX], gate_s[TMAX], Gp[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {
     beta_s[t] = t < T ? load_bf16_uniform(bg + (tok0 + t) * hv + h) : 0.f;
@@ -96,12 +128,13 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   }
 
   // 2. window operands and the committed history [0, n): HBM -> LDS, asynchronous
-  dma_rows(qg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, DK * 2, T, xkq);
-  dma_rows(kg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, DK * 2, T, xkq + T * DK);
+  dma_rows_256(qg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, T, xkq, KS * 2);
+  dma_rows_256(kg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, T, xkq + T * KS, KS * 2);
   dma_rows(vg + (tok0 * hv + h) * dv + col0, (size_t)hv * dv * 2, BV * 2, T, xv);
-  if (KDA) dma_rows(gg + (tok0 * hv + h) * DK, (size_t)hv * DK * 2, DK * 2, T, xg);
+  if (KDA) dma_rows_256(gg + (tok0 * hv + h) * DK, (size_t)hv * DK * 2, T, xg, KS * 2);
   if (nh > 0) {
-    dma_rows(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, DK * 2, nh, hkeys);
+    dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, nh, hkeys,
+                 KS * 2);
     dma_rows(a.ring_d + ((size_t)slot * L * hv + h) * dv + col0, (size_t)hv * dv * 4, BV * 4,
              nh, hd);
     if (KDA)
@@ -117,144 +150,245 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[j][i] = load4(sg + (size_t)(4 * (rg + RG * j) + i) * dv + 4 * cc);
+    for (int i = 0; i < 4; ++i)
+      s[j][i] = load4_nt(sg + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc));
   }
   code_fence();
-
-  if (tid == 0) {
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      if (t < T) {
-        bw[t] = beta_s[t];
-        gw[t] = gate_s[t];
-      }
-    }
-  }
   lds_barrier<QPT * 4>();                                // every copy but the tile is in LDS
 
-  // 4. decays: window prefix products and scaled window vectors; history suffix products
-  if (tid < DK) {
-    float run = 1.f;
-    for (int t = 0; t < T; ++t) {
-      run *= KDA ? to_f32(xg[t * DK + tid]) : gw[t];
-      xs[t * XS + tid] = run * to_f32(xkq[t * DK + tid]);
-      xs[(T + t) * XS + tid] = run * to_f32(xkq[(T + t) * DK + tid]);
-    }
-    for (int m = 2 * T; m < lay.nvec_pad; ++m) xs[m * XS + tid] = 0.f;
-    if (KDA) {
-      float g = 1.f;
-      for (int i = nh - 1; i >= 0; --i) {
-        khat[i * XS + tid] = g * to_f32(hkeys[i * DK + tid]);
-        g *= hg[i * DK + tid];
-      }
-      Gam[tid] = g;
+  const int nvec = 2 * T, hrows = fold ? 0 : nh;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // 4. decays and readout vectors (q_t at row 2t, k_t at row 2t+1).  GDN: window prefix
+  // decays Gp[t] = prod_{w<=t} alpha_w from the gate registers, total history decay Gam,
+  // suffix decay of each record; KDA: per key channel, in LDS.
+  float Gam = 1.f;
+  {
+    float g = 1.f;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      g *= gate_s[t];
+      Gp[t] = g;
     }
   }
   if (!KDA) {
-    // gamma_i = prod_{i<j<nh} alpha_j, each thread on its own record; Gam = gamma_0 alpha_0
-    const int i = kThreads - 1 - tid;
-    if (i < nh) {
-      float g = 1.f;
-      for (int j = i + 1; j < nh; ++j) g *= hg[j];
-      gam_i[i] = g;
-      if (i == 0) Gam[0] = g * hg[0];
+    for (int i = 0; i < nh; ++i) Gam *= hg[i];
+    if (tid < DK) {
+      float xq[TMAX], xk[TMAX];
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {                   // rows < 2*TMAX: in bounds
+        xq[t] = to_f32(xkq[t * KS + tid]);
+        xk[t] = to_f32(xkq[(T + t) * KS + tid]);
+      }
+      const float scale = fold ? 1.f : Gam;
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+          xr[(2 * t) * XS + tid] = (scale * Gp[t]) * xq[t];
+          xr[(2 * t + 1) * XS + tid] = (scale * Gp[t]) * xk[t];
+        }
+      }
+      for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
+    } else {
+      for (int i = tid - DK; i < nh; i += kThreads - DK) {
+        float g = 1.f;
+        for (int j = i + 1; j < nh; ++j) g *= hg[j];
+        gam_i[i] = g;
+      }
     }
-    if (nh == 0 && tid == kThreads - 1) Gam[0] = 1.f;
+  } else {
+    if (tid < DK) {
+      float run = 1.f;
+      for (int t = 0; t < T; ++t) {
+        run *= to_f32(xg[t * KS + tid]);
+        const float q = run * to_f32(xkq[t * KS + tid]);
+        const float k = run * to_f32(xkq[(T + t) * KS + tid]);
+        xs[t * XS + tid] = q;
+        xs[(T + t) * XS + tid] = k;
+      }
+      float g = 1.f;
+      for (int i = nh - 1; i >= 0; --i) {
+        khat[i * XS + tid] = g * to_f32(hkeys[i * KS + tid]);
+        g *= hg[i * DK + tid];
+      }
+      Gamv[tid] = g;
+      const float scale = fold ? 1.f : g;
+      for (int t = 0; t < T; ++t) {
+        xr[(2 * t) * XS + tid] = scale * xs[t * XS + tid];
+        xr[(2 * t + 1) * XS + tid] = scale * xs[(T + t) * XS + tid];
+      }
+      for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
-  // 5. readout vectors, window pair scalars, history scores
-  if (!fold && tid < DK) {
-    const float G = KDA ? Gam[tid] : Gam[0];
-    for (int m = 0; m < lay.nvec_pad; ++m) xr[m * XS + tid] = G * xs[m * XS + tid];
-  }
-  {
-    const int npair = T * T, ndots = npair + (fold ? 0 : nh * 2 * T);
-    for (int d = tid; d < ndots; d += kThreads) {
-      if (d < npair) {
-        const int t = d / T, u = d - t * T;
-        if (u <= t) {
-          const bf16* qt = xkq + t * DK;
-          const bf16* kt = xkq + (T + t) * DK;
-          const bf16* ku = xkq + (T + u) * DK;
-          float sq = 0.f, sk = 0.f;
-          if (KDA) {
-            for (int r = 0; r < DK; r += 4) {
-              f4 dec = f4{1.f, 1.f, 1.f, 1.f};
-              for (int w = u + 1; w <= t; ++w) dec *= bf16x4(xg + w * DK + r);
-              const f4 kd = bf16x4(ku + r) * dec;
-              const f4 a4 = bf16x4(qt + r) * kd, b4 = bf16x4(kt + r) * kd;
-              sq += (a4[0] + a4[1]) + (a4[2] + a4[3]);
-              sk += (b4[0] + b4[1]) + (b4[2] + b4[3]);
-            }
-          } else {
-            float dec = 1.f;
-            for (int w = u + 1; w <= t; ++w) dec *= gw[w];
-            for (int r = 0; r < DK; r += 4) {
-              const f4 k4 = bf16x4(ku + r);
-              const f4 a4 = bf16x4(qt + r) * k4, b4 = bf16x4(kt + r) * k4;
-              sq += (a4[0] + a4[1]) + (a4[2] + a4[3]);
-              sk += (b4[0] + b4[1]) + (b4[2] + b4[3]);
-            }
-            sq *= dec;
-            sk *= dec;
-          }
-          Qm[t * TMAX + u] = sq;
-          if (u < t) Am[t * TMAX + u] = bw[t] * sk;
+  // 5. scores.  Rows: history records 0..hrows-1 (not on a fold), then (GDN) the window
+  // keys; columns: the window vectors q_0..q_{T-1}, k_0..k_{T-1}.
+  if (!KDA) {
+    // undecayed dot products; the decays are applied where the scores are used
+    const int R = hrows + T, RT = (R + 15) >> 4, CT = (nvec + 15) >> 4;   // CT is 1 or 2
+    for (int tile = wave; tile < RT * CT; tile += kWaves) {
+      const int rt = CT == 1 ? tile : tile >> 1, ct = CT == 1 ? 0 : tile & 1;
+      const int ra = rt * 16 + l16, m = ct * 16 + l16;
+      const bool aok = ra < R, bok = m < nvec;
+      // operands from rows that always exist; rows outside the tile are selected away
+      const bf16* ap = ra < hrows ? hkeys + ra * KS : xkq + (T + (aok ? ra - hrows : 0)) * KS;
+      const bf16* bp = xkq + (bok ? m : 0) * KS;
+      const s4 zero = s4{0, 0, 0, 0};
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {              // two batches of LDS reads
+        s4 av[DK / 32], bv[DK / 32];
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+          const int k0 = (half * (DK / 32) + kb) * 16 + 4 * g4;
+          av[kb] = *reinterpret_cast<const s4*>(ap + k0);
+          bv[kb] = *reinterpret_cast<const s4*>(bp + k0);
         }
-      } else {
-        const int e = d - npair, i = e / (2 * T), m = e - i * (2 * T);
-        const float* xm = xs + m * XS;
-        float sc = 0.f;
-        if (KDA) {
-          const float* ki = khat + i * XS;
-          for (int r = 0; r < DK; r += 4) {
-            const f4 p4 = load4(ki + r) * load4(xm + r);
-            sc += (p4[0] + p4[1]) + (p4[2] + p4[3]);
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+          acc = mfma_bf16_16x16x16(aok ? av[kb] : zero, bok ? bv[kb] : zero, acc);
+      }
+      if (bok) {
+        const bool isq = m < T;
+        const int t = isq ? m : m - T;
+        const int r0 = rt * 16 + 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = r0 + j;
+          if (rr < hrows) {
+            Cs[rr * CS + m] = acc[j];
+          } else if (rr < R) {
+            const int u = rr - hrows;
+            const float dec = gate_product(gate_s, u, t);
+            if (isq) {
+              if (u <= t) Qm[t * TMAX + u] = acc[j] * dec;
+            } else if (u < t) {
+              Am[t * TMAX + u] = pick(beta_s, t) * (acc[j] * dec);
+            }
           }
-        } else {
-          const bf16* ki = hkeys + i * DK;
-          for (int r = 0; r < DK; r += 4) {
-            const f4 p4 = bf16x4(ki + r) * load4(xm + r);
-            sc += (p4[0] + p4[1]) + (p4[2] + p4[3]);
-          }
-          sc *= gam_i[i];
         }
-        Cs[i * CS + m] = sc;
+      }
+    }
+  } else {
+    // history scores: fp32 MFMAs, wave w sums dk entries [32w, 32w + 32)
+    const int RT = (hrows + 15) >> 4, CT = (nvec + 15) >> 4;
+    for (int tile = 0; tile < RT * CT; ++tile) {
+      const int rt = CT == 1 ? tile : tile >> 1, ct = CT == 1 ? 0 : tile & 1;
+      const int ra = rt * 16 + l16, m = ct * 16 + l16;
+      const bool aok = ra < hrows, bok = m < nvec;
+      const float* ap = khat + (aok ? ra : 0) * XS;
+      const float* bp = xs + (bok ? m : 0) * XS;
+      float av[8], bv[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        av[st] = ap[32 * wave + 4 * st + g4];
+        bv[st] = bp[32 * wave + 4 * st + g4];
+      }
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) acc = mfma_16x16x4(aok ? av[st] : 0.f, bok ? bv[st] : 0.f, acc);
+      float* part = Cs + wave * lay.lp * CS;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[(rt * 16 + 4 * g4 + j) * CS + m] = acc[j];
+    }
+    // window pairs: per-channel decays between u and t, 16 lanes per pair
+    const int npair = T * (T + 1) / 2, grp = tid >> 4, e = tid & 15;
+    for (int p = grp; p < npair; p += kThreads / 16) {
+      int t = 0;
+      while ((t + 1) * (t + 2) / 2 <= p) ++t;
+      const int u = p - t * (t + 1) / 2;
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 2; ++c4) {
+        const int r = 8 * e + 4 * c4;
+        f4 dec = f4{1.f, 1.f, 1.f, 1.f};
+        for (int w = u + 1; w <= t; ++w) dec *= bf16x4(xg + w * KS + r);
+        const f4 kd = bf16x4(xkq + (T + u) * KS + r) * dec;
+        const f4 a4 = bf16x4(xkq + t * KS + r) * kd, b4 = bf16x4(xkq + (T + t) * KS + r) * kd;
+        sq += (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        sk += (b4[0] + b4[1]) + (b4[2] + b4[3]);
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        sq += __shfl_xor(sq, off);
+        sk += __shfl_xor(sk, off);
+      }
+      if (e == 0) {
+        Qm[t * TMAX + u] = sq;
+        if (u < t) Am[t * TMAX + u] = pick(beta_s, t) * sk;
       }
     }
   }
   lds_barrier();
 
-  // This workgroup has read every ring record it needs (the copies have landed in LDS).
-  // On a fused fold the window's keys and gates go to rows 0..T-1, which other workgroups
-  // of the key group may still read: only the last of them to get here writes them (no
-  // spinning).  Only read-before-write ordering is at stake, no data passes through the
-  // counter: every increment follows its workgroup's completed reads, and the writes
-  // follow the return of the last increment, so a relaxed device-scope atomic suffices.
-  // The flag reaches the other threads through the barriers of the readout.
-  if (fold && tid == 0) {
-    const int old = __hip_atomic_fetch_add(a.group_counter + (size_t)row * hk + kh, 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    flags[0] = (old == a.G * a.NV - 1);
+  // 6. history part of the readout, before the tile is touched: wave w sums
+  // d_i[c] C[i][m] over the records i = w, w + 4, ... into its partial red[w][m][c]
+  // (vectors in readout order), to which step 8 adds the wave's tile part
+  const int NP = lay.nvec_pad;
+  if (hrows > 0) {
+    for (int c = lane; c < BV; c += 64) {
+      float hP[NV2];
+#pragma unroll
+      for (int m = 0; m < NV2; ++m) hP[m] = 0.f;
+      for (int i = wave; i < hrows; i += kWaves) {
+        const float di = hd[i * BV + c];
+        const float w = KDA ? di : di * gam_i[i];
+#pragma unroll
+        for (int m = 0; m < NV2; ++m) {
+          if (m < nvec) {
+            const int t = m >> 1, col = (m & 1) ? T + t : t;   // score column of vector m
+            float cm = Cs[i * CS + col];
+            if (KDA) {
+              const int plane = lay.lp * CS;
+              cm = (cm + Cs[plane + i * CS + col]) +
+                   (Cs[2 * plane + i * CS + col] + Cs[3 * plane + i * CS + col]);
+            }
+            hP[m] = fmaf(w, cm, hP[m]);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NV2; ++m)
+        if (m < nvec) red[(wave * NP + m) * BV + c] = KDA ? hP[m] : hP[m] * Gp[m >> 1];
+    }
   }
 
-  // 6. rows that overflow: fold the prefix into the registers and write the state once
+  // the partials above are read back by other lanes of the same wave in step 8: LDS
+  // operations of a wave complete in order, so only compiler reordering must be ruled out
+  asm volatile("" ::: "memory");
+
+  // 7. rows that overflow.  On a fused fold the window's keys and gates go to rows
+  // 0..T-1, which other workgroups of the key group may still read: only the last of
+  // them to get past its copies writes them (no spinning).  Only read-before-write
+  // ordering is at stake, no data passes through the counter: every increment follows
+  // its workgroup's completed reads (the copies landed before the first barrier), and the
+  // writes follow the return of the last increment, so a relaxed device-scope atomic
+  // suffices.  Wave 0 increments and later writes.  (Its wait for the returned value also
+  // waits for the tile, as vector-memory operations complete in order: hence here.)
+  int last = 0;
+  if (fold && wave == 0) {
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(a.group_counter + (size_t)row * hk + kh, 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = __shfl(old, 0) == a.G * a.NV - 1;
+  }
   if (fold) {
-    const float G0 = KDA ? 0.f : Gam[0];
+    // S <- Gam (.) S + sum_i gamma_i k_i d_i^T in the registers, then one write
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       const int r0 = 4 * (rg + RG * j);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[j][i] *= KDA ? Gam[r0 + i] : G0;
+      for (int i = 0; i < 4; ++i) s[j][i] *= KDA ? Gamv[r0 + i] : Gam;
     }
+#pragma unroll 4
     for (int i = 0; i < nh; ++i) {
-      const f4 dq = load4(hd + i * BV + 4 * cc);
-      const float gi = KDA ? 1.f : gam_i[i];
+      const f4 dq = load4(hd + i * BV + 4 * cc) * (KDA ? 1.f : gam_i[i]);
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
         const int r0 = 4 * (rg + RG * j);
-        const f4 kq = KDA ? load4(khat + i * XS + r0) : bf16x4(hkeys + i * DK + r0) * gi;
+        const f4 kq = KDA ? load4(khat + i * XS + r0) : bf16x4(hkeys + i * KS + r0);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) s[j][ii] += kq[ii] * dq;
       }
@@ -264,72 +398,65 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
     for (int j = 0; j < QPT; ++j) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        store4(so + (size_t)(4 * (rg + RG * j) + i) * dv + 4 * cc, s[j][i]);
+        store4_nt(so + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc), s[j][i]);
         s[j][i] = round4<ST>(s[j][i]);
       }
     }
   }
 
-  // 7. readout P[m][c] = H^T x_m over the tile registers (+ history scores), reduced over
-  // the row groups of a wave by butterflies, then over the 4 waves through LDS
-  const float* xv_read = fold ? xs : xr;
-  const int nvec = 2 * T;
-  for (int m0 = 0; m0 < nvec; m0 += VPP) {
+  // 8. tile part of the readout, S^T xr_m over this thread's rows, summed over the row
+  // groups of the wave by lane shuffles; one partial per wave goes to LDS
+#pragma unroll
+  for (int ps = 0; ps < NPASS; ++ps) {
+    const int m0 = ps * VPP;
+    if (m0 >= nvec) break;
     f4 acc[VPP];
 #pragma unroll
-    for (int m = 0; m < VPP; ++m) acc[m] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int mm = 0; mm < VPP; ++mm) acc[mm] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       const int rq = rg + RG * j;
 #pragma unroll
-      for (int m = 0; m < VPP; ++m) {
-        const f4 x = load4(xv_read + (m0 + m) * XS + 4 * rq);
-        acc[m] += s[j][0] * x[0];
-        acc[m] += s[j][1] * x[1];
-        acc[m] += s[j][2] * x[2];
-        acc[m] += s[j][3] * x[3];
-      }
-    }
-    if (!fold) {
-      for (int i = rg; i < nh; i += RG) {
-        const f4 dq = load4(hd + i * BV + 4 * cc);
-#pragma unroll
-        for (int m = 0; m < VPP; ++m) {
-          const float c = (m0 + m < nvec) ? Cs[i * CS + m0 + m] : 0.f;
-          acc[m] += dq * c;
-        }
+      for (int mm = 0; mm < VPP; ++mm) {
+        const f4 x = load4(xr + (m0 + mm) * XS + 4 * rq);
+        acc[mm] += s[j][0] * x[0];
+        acc[mm] += s[j][1] * x[1];
+        acc[mm] += s[j][2] * x[2];
+        acc[mm] += s[j][3] * x[3];
       }
     }
 #pragma unroll
     for (int off = CC; off < 64; off <<= 1) {
 #pragma unroll
-      for (int m = 0; m < VPP; ++m) {
+      for (int mm = 0; mm < VPP; ++mm) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[m][jj] += __shfl_xor(acc[m][jj], off);
+        for (int jj = 0; jj < 4; ++jj) acc[mm][jj] += __shfl_xor(acc[mm][jj], off);
       }
     }
     if (lane < CC) {
+      // this wave's history partial for these columns was written by lanes of this same
+      // wave, earlier in program order
 #pragma unroll
-      for (int m = 0; m < VPP; ++m) store4(red + (wave * VPP + m) * BV + 4 * cc, acc[m]);
+      for (int mm = 0; mm < VPP; ++mm) {
+        float* r = red + (wave * NP + m0 + mm) * BV + 4 * cc;
+        store4(r, (hrows > 0 && m0 + mm < nvec) ? acc[mm] + load4(r) : acc[mm]);
+      }
     }
-    lds_barrier();
-    for (int i = tid; i < VPP * BV; i += kThreads) {
-      const int m = i / BV, c = i - m * BV;
-      if (m0 + m < nvec)
-        P[(m0 + m) * BV + c] = (red[m * BV + c] + red[(VPP + m) * BV + c]) +
-                               (red[(2 * VPP + m) * BV + c] + red[(3 * VPP + m) * BV + c]);
-    }
-    lds_barrier();
   }
+  lds_barrier();
 
-  // 8. per column: forward substitution over the window, outputs, ring deltas
+  // 9. per column: the readout (sum of the 4 wave partials), forward
+  // substitution over the window, outputs, ring deltas
   if (tid < BV) {
     const int c = tid, col = col0 + c;
     float d[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        float U = bw[t] * (to_f32(xv[t * BV + c]) - P[(T + t) * BV + c]);
+        const int m = 2 * t + 1;
+        const float pk = ((red[m * BV + c] + red[(NP + m) * BV + c]) +
+                          (red[(2 * NP + m) * BV + c] + red[(3 * NP + m) * BV + c]));
+        float U = beta_s[t] * (to_f32(xv[t * BV + c]) - pk);
 #pragma unroll
         for (int u = 0; u < t; ++u) U = fmaf(-Am[t * TMAX + u], d[u], U);
         d[t] = U;
@@ -338,7 +465,9 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        float o = P[t * BV + c];
+        const int m = 2 * t;
+        float o = ((red[m * BV + c] + red[(NP + m) * BV + c]) +
+                   (red[(2 * NP + m) * BV + c] + red[(3 * NP + m) * BV + c]));
 #pragma unroll
         for (int u = 0; u <= t; ++u) o = fmaf(Qm[t * TMAX + u], d[u], o);
         a.out[((tok0 + t) * hv + h) * dv + col] = o;
@@ -346,33 +475,36 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
       }
     }
   }
-  if (a.write_pos_out && h == 0 && vt == 0 && tid == 0) a.write_pos_out[row] = base;
 
-  // 9. the window's keys and gates (shared by the key group / by the head's tiles)
-  const bool writer = fold ? (flags[0] != 0) : (h % a.G == 0 && vt == 0);
-  if (writer) {
-    bf16* rk = static_cast<bf16*>(a.ring_k);
-    for (int i = tid; i < T * (DK / 8); i += kThreads) {        // 16-byte chunks
-      const int t = i / (DK / 8), c8 = (i - t * (DK / 8)) * 8;
-      *reinterpret_cast<uint4*>(rk + (((size_t)slot * L + base + t) * hk + kh) * DK + c8) =
-          *reinterpret_cast<const uint4*>(xkq + (T + t) * DK + c8);
-    }
-    if (KDA) {
-      for (int i = tid; i < T * DK; i += kThreads) {
-        const int t = i / DK, r = i - t * DK;
-        a.ring_g[(((size_t)slot * L + base + t) * hv + h) * DK + r] = to_f32(xg[t * DK + r]);
+  // 10. wave 0: write_pos, and the window's keys and gates (shared by the key group / by
+  // the head's tiles)
+  if (wave == 0) {
+    if (a.write_pos_out && h == 0 && vt == 0 && lane == 0) a.write_pos_out[row] = base;
+    const bool writer = fold ? (last != 0) : (h % a.G == 0 && vt == 0);
+    if (writer) {
+      bf16* rk = static_cast<bf16*>(a.ring_k);
+      for (int i = lane; i < T * (DK / 8); i += 64) {           // 16-byte chunks
+        const int t = i / (DK / 8), c8 = (i - t * (DK / 8)) * 8;
+        *reinterpret_cast<uint4*>(rk + (((size_t)slot * L + base + t) * hk + kh) * DK + c8) =
+            *reinterpret_cast<const uint4*>(xkq + (T + t) * KS + c8);
       }
-    } else if (tid == 0) {
-      for (int t = 0; t < T; ++t)
-        for (int g = 0; g < a.G; ++g) {
-          const int hh = kh * a.G + g;
-          a.ring_g[((size_t)slot * L + base + t) * hv + hh] =
-              load_bf16_uniform(gg + (tok0 + t) * hv + hh);
+      if (KDA) {
+        for (int i = lane; i < T * DK; i += 64) {
+          const int t = i / DK, r = i - t * DK;
+          a.ring_g[(((size_t)slot * L + base + t) * hv + h) * DK + r] = to_f32(xg[t * KS + r]);
         }
+      } else if (lane == 0) {
+        for (int t = 0; t < T; ++t)
+          for (int g = 0; g < a.G; ++g) {
+            const int hh = kh * a.G + g;
+            a.ring_g[((size_t)slot * L + base + t) * hv + hh] =
+                load_bf16_uniform(gg + (tok0 + t) * hv + hh);
+          }
+      }
+      if (fold && lane == 0)
+        __hip_atomic_store(a.group_counter + (size_t)row * hk + kh, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (fold && tid == 0)
-      __hip_atomic_store(a.group_counter + (size_t)row * hk + kh, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

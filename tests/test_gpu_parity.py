@@ -93,6 +93,17 @@ def test_tile_widths(tile_v):
     _run(REDUCED['c1'].with_(steps=18), tile_v=tile_v)
 
 
+@pytest.mark.parametrize('name,cfg', [
+    ('c1', REDUCED['c1'].with_(B=16, steps=18)),
+    ('c3', REDUCED['c3'].with_(B=8, steps=10)),
+])
+def test_key_group_xcd_order(name, cfg):
+    """Batch * key heads a multiple of 8: the verify hands whole key groups to the XCDs in
+    turn (the other tests take the contiguous order)."""
+    assert (cfg.B * cfg.hk) % 8 == 0
+    _run(cfg)
+
+
 def test_odd_shapes():
     """dk=dv=16 (one 16-wide tile), dv=48 (three 16-wide tiles), dk=64, ring == window."""
     _run(W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=16, dv=48, L=3, T=3, accept=('uniform', 0, 3),
