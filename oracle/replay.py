@@ -9,8 +9,9 @@ Method (the three pages, read together):
     (sglang GDN ReplaySSM spec-verify PR, commit 1) after replaying the committed
     history over S (commit 5: history terms, skipped when write_pos is 0).
   * When the next verify would exceed the ring, the whole prefix is folded into S first,
-    inside the verify (LightLLM: lazy compaction "when the next verify would exceed
-    capacity", decided on device; PR description: fold fused into the decode kernel).
+    inside the verify (LightLLM commit messages: compaction is lazy and triggered by a
+    verify that would not fit, a decision taken on the device; PR description: the fold
+    runs inside the decode kernel).
     Then write_pos = 0.
   * After every layer of a step, the shared cursor advances by the accept length (the
     rejected tail is trimmed; LightLLM commits on the shared cursor being advanced only
