@@ -19,6 +19,12 @@ cursor model: state read, inputs, history records read, outputs and ring writes,
 state write of rows that fold) / mean launch time from HIP events on the launch stream
 around every verify of the timed steps.  cpu_baseline: the fp64 oracle on a bounded
 sample of the same workload, single-threaded.
+
+extra: the T = 3 case; the T = 1 verify at three history states (none, steady, every row
+folding); and full step loops (verify per layer, cursor advance, commit folds by policy)
+of the spec-verify (batch 128, bf16 state, T = 4, fold every commit), KDA (batch 64, T = 3)
+and large-ring (batch 256, ring 64, T = 8, 4 layers, forced commit folds) workloads, each
+with verify and commit-fold kernel times and verified / committed tokens per second.
 """
 from __future__ import annotations
 
@@ -244,6 +250,164 @@ def cpu_baseline(T: int, budget_s: float = 12.0):
                       f'{steps} decode steps of one layer, {elapsed:.1f} s, fp64 numpy'}
 
 
+# ----------------------------------------------------------------------------- more workloads
+# Timing only: the other workloads and the history states run on random device-side data of
+# the same shapes and distributions (unit q/k rows, v ~ N(0,1), beta ~ U(0,1), gates
+# exp(-softplus(N(0,1)))), so that the benchmark does not spend minutes building fp64 data.
+
+def _rand_setup(cfg, layers, seed=1234):
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    dev = torch.device('cuda:0')
+    g = torch.Generator(device=dev).manual_seed(seed)
+    bf, f32 = torch.bfloat16, torch.float32
+    sd = bf if cfg.state_dtype == 'bf16' else f32
+    ns, L = cfg.num_slots, cfg.L
+
+    def unit(*shape):
+        x = torch.randn(*shape, generator=g, device=dev)
+        return x / x.norm(dim=-1, keepdim=True)
+
+    def gates(*shape):
+        return torch.exp(-torch.nn.functional.softplus(torch.randn(*shape, generator=g, device=dev)))
+
+    gsh = (cfg.hv, cfg.dk) if cfg.kda else (cfg.hv,)
+    st = dict(
+        S=[(torch.randn(ns, cfg.hv, cfg.dk, cfg.dv, generator=g, device=dev) * 0.05).to(sd)
+           for _ in range(layers)],
+        rk=[unit(ns, L, cfg.hk, cfg.dk).to(bf) for _ in range(layers)],
+        rd=[torch.randn(ns, L, cfg.hv, cfg.dv, generator=g, device=dev) * 0.5 for _ in range(layers)],
+        rg=[gates(ns, L, *gsh) for _ in range(layers)])
+    BT = cfg.B * cfg.T
+
+    def inputs():
+        return (unit(BT, cfg.hk, cfg.dk).to(bf), unit(BT, cfg.hk, cfg.dk).to(bf),
+                torch.randn(BT, cfg.hv, cfg.dv, generator=g, device=dev).to(bf),
+                torch.rand(BT, cfg.hv, generator=g, device=dev).to(bf),
+                gates(BT, *gsh).to(bf))
+    slots_np = W.slot_map(cfg)
+    d = rs.Dims(cfg.B, cfg.T, cfg.hk, cfg.hv, cfg.dk, cfg.dv, L, ns, rs.BF16,
+                rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, 0)
+    st.update(slots_np=slots_np, slots=torch.from_numpy(slots_np.astype(np.int32)).to(dev),
+              inputs=inputs, d=d, dev=dev)
+    return st
+
+
+def history_states(iters=60, layers=8):
+    """The decode verify (T = 1) at three history states, cursors held fixed: no history
+    (every write_pos 0), steady (cursor = row mod 16, the benchmark's spread), and every
+    row folding in the verify (cursor = 16).  Kernel time from HIP events on the stream."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    cfg = W.CONFIGS['c1']
+    st = _rand_setup(cfg, layers)
+    dev, slots_np = st['dev'], st['slots_np']
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+    out = torch.empty(cfg.B, cfg.hv, cfg.dv, device=dev)
+    counter = torch.zeros(cfg.B * cfg.hk, dtype=torch.int32, device=dev)
+    ins = st['inputs']()
+    res = {}
+    for name in ('no_history', 'steady', 'all_fold'):
+        cur = np.zeros(cfg.num_slots, np.int32)
+        for r in live:
+            cur[slots_np[r]] = 0 if name == 'no_history' else (r % cfg.L if name == 'steady' else cfg.L)
+        cursor = torch.from_numpy(cur).to(dev)
+        calls = [rs.prepare_verify(False, st['d'], *ins, st['S'][l], st['rk'][l], st['rd'][l],
+                                   st['rg'][l], cursor, st['slots'], out, None, counter)
+                 for l in range(layers)]
+        stream = torch.cuda.current_stream()
+        for i in range(16):
+            calls[i % layers](stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            calls[i % layers](stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        n = [int(cur[slots_np[r]]) for r in live]
+        byts = verify_bytes(cfg, n, [x + 1 > cfg.L for x in n])
+        res[name] = {'kernel_us': round(us, 3), 'achieved_gbs': round(byts / us / 1e3, 1),
+                     'frac': round(byts / us / 1e3 / HBM_PEAK_GBS, 4), 'bytes_per_launch': byts}
+    return res
+
+
+def run_workload(name, steps=30, warmup=10):
+    """A full step loop of another workload: a verify per layer, the cursor advance, and the
+    commit folds its policy asks for.  Verify and commit-fold kernel times from HIP events;
+    verified tokens/s per layer = live * T * layers / step time; committed tokens/s per
+    layer = accepted tokens / step time."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    cfg = W.CONFIGS[name]
+    layers = cfg.layers
+    st = _rand_setup(cfg, layers)
+    dev, slots_np, d = st['dev'], st['slots_np'], st['d']
+    cursor = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
+    fold_len = torch.zeros_like(cursor)
+    counter = torch.zeros(cfg.B * cfg.hk, dtype=torch.int32, device=dev)
+    out = torch.empty(cfg.B * cfg.T, cfg.hv, cfg.dv, device=dev)
+    n_sets = 4
+    sets = [st['inputs']() for _ in range(n_sets)]
+    verify = [[rs.prepare_verify(cfg.kda, d, *sets[j], st['S'][l], st['rk'][l], st['rd'][l],
+                                 st['rg'][l], cursor, st['slots'], out, None, counter)
+               for l in range(layers)] for j in range(n_sets)]
+    commit = [rs.prepare_commit_fold(d, cfg.kda, st['S'][l], st['rk'][l], st['rd'][l],
+                                     st['rg'][l], fold_len, st['slots']) for l in range(layers)]
+    total = warmup + steps
+    accs = [W.accept_lengths(cfg, j) for j in range(total)]
+    acc_d = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in accs]
+    pols = [W.step_policy(cfg, j) for j in range(total)]
+    adv = [rs.prepare_cursor_advance(d, cursor, fold_len, st['slots'], acc_d[j], pols[j][0],
+                                     pols[j][1]) for j in range(total)]
+    stream = torch.cuda.current_stream()
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+    ev_v, ev_c = [], []
+
+    def step(j, timed):
+        for l in range(layers):
+            if timed:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record(stream)
+            verify[j % n_sets][l](stream)
+            if timed:
+                e[1].record(stream)
+                ev_v.append(e)
+        adv[j](stream)
+        if pols[j][0] != rs.FOLD_NONE:
+            for l in range(layers):
+                if timed:
+                    e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    e[0].record(stream)
+                commit[l](stream)
+                if timed:
+                    e[1].record(stream)
+                    ev_c.append(e)
+
+    for j in range(warmup):
+        step(j, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(warmup, total):
+        step(j, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / steps
+    acc_per_step = float(np.mean([sum(int(accs[j][r]) for r in live) for j in range(warmup, total)]))
+    res = {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'ring': cfg.L, 'layers': layers,
+           'kda': cfg.kda, 'state': cfg.state_dtype, 'ms_per_step': round(step_s * 1e3, 5),
+           'verified_tokens_per_s_per_layer': round(len(live) * cfg.T * layers / step_s / layers, 1),
+           'committed_tokens_per_s_per_layer': round(acc_per_step / step_s, 1),
+           'verify_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_v])) * 1e3, 3)}
+    if ev_c:
+        res['commit_fold_us'] = round(float(np.mean([a.elapsed_time(b) for a, b in ev_c])) * 1e3, 3)
+        res['commit_folds_per_step'] = round(len(ev_c) / steps, 3)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -257,6 +421,10 @@ def main():
                     help='print the hash of the verify kernel sources and exit')
     ap.add_argument('--copy-calibration', action='store_true',
                     help='first run plain copies of 256 MiB (for counter calibration)')
+    ap.add_argument('--no-extra', action='store_true',
+                    help='skip the history states and the other workloads')
+    ap.add_argument('--only-workload', default='',
+                    help='run one of the other workloads (c2, c3, c4) alone and exit')
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -268,6 +436,9 @@ def main():
               'no exchange inside it, so one GPU shows the per-GPU kernel.', file=sys.stderr)
         sys.exit(2)
 
+    if args.only_workload:
+        print(json.dumps(run_workload(args.only_workload)), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration()
     Ts = [args.only_T] if args.only_T else [1, 3]
@@ -313,6 +484,12 @@ def main():
                           'achieved_gbs': round(r['achieved_gbs'], 1),
                           'frac': round(r['achieved_gbs'] / HBM_PEAK_GBS, 4),
                           'bytes_per_launch': int(r['bytes_per_launch'])}
+    if not args.no_extra:
+        extra['history_states_T1'] = history_states()
+        print(f'# history states: {extra["history_states_T1"]}', file=sys.stderr, flush=True)
+        for name in ('c2', 'c3', 'c4'):
+            extra[name] = run_workload(name)
+            print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
     if extra:
         line['extra'] = extra
     if not args.no_cpu_baseline:
