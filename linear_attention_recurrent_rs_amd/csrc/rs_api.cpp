@@ -40,8 +40,8 @@ int choose_bv(const rs_dims* d) {
   return 16;
 }
 
-// The dk = 128 / bf16-input verify (rs_verify_fast.hip) covers the tile widths 32, 64
-// and 128; every other shape takes the general verify (rs_kernels.hip).
+// The dk = 128 / bf16-input kernels (rs_verify_fast.hip, rs_fold_fast.hip) cover the tile
+// widths 32, 64 and 128; every other shape takes the general kernels (rs_kernels.hip).
 bool use_fast(const rs_dims* d, int bv) {
   return d->dk == 128 && d->act_dtype == RS_BF16 && (bv == 32 || bv == 64 || bv == 128);
 }
@@ -109,12 +109,22 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   const bool kda = is_kda != 0;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
   int bv = choose_bv(d);
-  rs::LdsLayout lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
-  while (lay.total > kMaxLds && d->tile_v == 0 && bv > 16) {
+  // dk = 128 with bf16 keys and an fp32 state: the register-tile MFMA fold
+  // (rs_fold_fast.hip).  A bf16 state would reach those registers by 8-byte loads, 32-byte
+  // row pieces per 16-column block, so it takes the LDS-staged fold (rs_kernels.hip).
+  const bool f32_state = d->state_dtype == RS_F32;
+  bool fast = false;
+  rs::FoldFastLayout flay{};
+  rs::LdsLayout lay{};
+  for (;;) {
+    fast = f32_state && use_fast(d, bv);
+    if (fast) flay = rs::fold_fast_layout(kda, bv, d->ring_cap);
+    else lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
+    const int lds = fast ? flay.total : lay.total;
+    if (lds <= kMaxLds || d->tile_v != 0 || bv <= 16) break;
     bv /= 2;
-    lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
   }
-  if (lay.total > kMaxLds) return RS_E_SHAPE;
+  if ((fast ? flay.total : lay.total) > kMaxLds) return RS_E_SHAPE;
   if (d->batch == 0) return RS_OK;
   if (!state_in || !state_out || !ring_k || !ring_d || !ring_g || !nrec || !slot_idx)
     return RS_E_NULLPTR;
@@ -124,8 +134,10 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   a.nblocks = d->batch * d->hv * a.NV;
   a.state_in = state_in; a.state_out = state_out; a.ring_k = ring_k; a.ring_d = ring_d;
   a.ring_g = ring_g; a.nrec = nrec; a.slot_idx = slot_idx; a.lay = lay;
-  hipError_t e = rs::launch_fold(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv,
-                                 materialize, a, stream);
+  hipError_t e = fast
+      ? rs::launch_fold_fast(kda, d->state_dtype == RS_BF16, bv, materialize, a, flay, stream)
+      : rs::launch_fold(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv,
+                        materialize, a, stream);
   return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
 }
 

@@ -1,0 +1,175 @@
+// Commit fold and materialize for dk = 128 with bf16 keys (the Qwen3.5-shaped GDN and KDA
+// layers), gfx950.
+//
+// Same method as fold_kernel in rs_kernels.hip: for a slot with nrec records,
+//   S <- Gam (.) S + sum_{i < nrec} khat_i d_i^T,  khat_i = gamma_i (.) k_i,
+// gamma_i = prod_{i<j<nrec} alpha_j, Gam = prod_{j<nrec} alpha_j (per key channel for KDA),
+// written back in place (commit fold, nrec = fold_len) or as an fp32 copy (materialize,
+// nrec = cursor).  The difference is where the tile lives: the [128 x BV] tile goes from
+// HBM (non-temporal loads) straight into fp32 MFMA accumulators, four consecutive
+// columns of one row per lane, and the rank-nrec update runs on v_mfma_f32_16x16x4_f32
+// with the records as the contraction index (A = d_i of 16 columns, B = khat_i of 16
+// rows).  Records come in by HBM->LDS copies; a wave owns 32 rows of the tile.  Records at
+// or past nrec are selected to zero before the MFMA, never read from the ring.
+#include <type_traits>
+
+#include "rs_device.h"
+#include "rs_internal.h"
+
+namespace rs {
+
+template <bool KDA, typename ST, typename OT, int BV, bool MATERIALIZE>
+__global__ __launch_bounds__(kThreads) void fold_fast_kernel(FoldArgs a, FoldFastLayout lay) {
+  constexpr int DK = 128, KS = kKeyStride;
+  constexpr int NCB = BV / 16;                 // 16-column blocks of the tile
+  constexpr int RBW = DK / 16 / kWaves;        // 16-row blocks per wave
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, q4 = lane >> 4;
+  const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
+  const int vt = lid % a.NV;
+  const int h = (lid / a.NV) % a.hv;
+  const int row = lid / (a.NV * a.hv);
+  const int slot = a.slot_idx[row];
+  if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
+  const int L = a.L, dv = a.dv, hv = a.hv, hk = a.hk;
+  int n = a.nrec[slot];
+  n = n < 0 ? 0 : (n > L ? L : n);
+  if (!MATERIALIZE && n == 0) return;                   // nothing to commit
+  const int kh = h / a.G, col0 = vt * BV;
+
+  bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
+  float* hd = reinterpret_cast<float*>(smem + lay.hd);
+  float* hg = reinterpret_cast<float*>(smem + lay.hg);
+  float* gam_i = reinterpret_cast<float*>(smem + lay.gam_i);
+  float* Gamv = reinterpret_cast<float*>(smem + lay.Gam);
+
+  // 1. records [0, n): keys, this tile's deltas, gates -> LDS, asynchronous
+  if (n > 0) {
+    const bf16* rkg = static_cast<const bf16*>(a.ring_k);
+    dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, n, hkeys,
+                 KS * 2);
+    dma_rows(a.ring_d + ((size_t)slot * L * hv + h) * dv + col0, (size_t)hv * dv * 4, BV * 4, n,
+             hd);
+    if (KDA)
+      dma_rows(a.ring_g + ((size_t)slot * L * hv + h) * DK, (size_t)hv * DK * 4, DK * 4, n, hg);
+    else
+      dma_words(a.ring_g + (size_t)slot * L * hv + h, (size_t)hv * 4, n, hg);
+  }
+  code_fence();
+
+  // 2. the state tile -> accumulators: lane holds row rb*16 + i16, columns cb*16 + 4*q4 ..+3
+  const ST* src =
+      static_cast<const ST*>(a.state_in) + (((size_t)slot * hv + h) * DK) * dv + col0;
+  f4 acc[RBW][NCB];
+#pragma unroll
+  for (int rbi = 0; rbi < RBW; ++rbi) {
+    const int r = (wave * RBW + rbi) * 16 + i16;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      acc[rbi][cb] = load4_nt(src + (uint32_t)(r * dv + cb * 16 + 4 * q4));
+  }
+  code_fence();
+  lds_barrier<RBW * NCB>();                              // the records are in LDS
+
+  // 3. decays.  GDN: Gam (every thread), gamma_i (thread i).  KDA: per key channel, the
+  // gates of record i are replaced in place by khat_i = gamma_i (.) k_i.
+  float Gam = 1.f;
+  if (!KDA) {
+    for (int i = 0; i < n; ++i) Gam *= hg[i];
+    for (int i = tid; i < n; i += kThreads) {
+      float g = 1.f;
+      for (int j = i + 1; j < n; ++j) g *= hg[j];
+      gam_i[i] = g;
+    }
+  } else if (tid < DK) {
+    float g = 1.f;
+    for (int i = n - 1; i >= 0; --i) {
+      const float al = hg[i * DK + tid];
+      hg[i * DK + tid] = g * to_f32(hkeys[i * KS + tid]);
+      g *= al;
+    }
+    Gamv[tid] = g;
+  }
+  lds_barrier();
+
+  // 4. S <- Gam (.) S, then the rank-n update on MFMA, four records per step
+#pragma unroll
+  for (int rbi = 0; rbi < RBW; ++rbi) {
+    const float gr = KDA ? Gamv[(wave * RBW + rbi) * 16 + i16] : Gam;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[rbi][cb] *= gr;
+  }
+  for (int ks = 0; ks < (n + 3) >> 2; ++ks) {
+    const int rec = 4 * ks + q4;
+    const bool ok = rec < n;
+    const int rs = ok ? rec : 0;                         // a row that exists; selected away
+    const float gsc = KDA ? 1.f : gam_i[rs];
+    float av[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const float dval = hd[rs * BV + cb * 16 + i16] * gsc;
+      av[cb] = ok ? dval : 0.f;
+    }
+#pragma unroll
+    for (int rbi = 0; rbi < RBW; ++rbi) {
+      const int r = (wave * RBW + rbi) * 16 + i16;
+      const float kv = KDA ? hg[rs * DK + r] : to_f32(hkeys[rs * KS + r]);
+      const float b = ok ? kv : 0.f;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[rbi][cb] = mfma_16x16x4(av[cb], b, acc[rbi][cb]);
+    }
+  }
+
+  // 5. one write: the state in place (its dtype, RNE) or the fp32 materialized copy
+  OT* dst = MATERIALIZE
+      ? static_cast<OT*>(a.state_out) + (((size_t)row * hv + h) * DK) * dv + col0
+      : static_cast<OT*>(a.state_out) + (((size_t)slot * hv + h) * DK) * dv + col0;
+#pragma unroll
+  for (int rbi = 0; rbi < RBW; ++rbi) {
+    const int r = (wave * RBW + rbi) * 16 + i16;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      store4_nt(dst + (uint32_t)(r * dv + cb * 16 + 4 * q4), acc[rbi][cb]);
+  }
+}
+
+template <bool KDA, typename ST, int BV, bool MAT>
+static hipError_t run_fold_fast(const FoldArgs& a, const FoldFastLayout& lay, hipStream_t s) {
+  using OT = typename std::conditional<MAT, float, ST>::type;
+  auto k = fold_fast_kernel<KDA, ST, OT, BV, MAT>;
+  if (lay.total > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), lay.total, s, a, lay);
+  return hipGetLastError();
+}
+
+template <bool KDA, typename ST, bool MAT>
+static hipError_t fold_fast_bv(int bv, const FoldArgs& a, const FoldFastLayout& lay,
+                               hipStream_t s) {
+  switch (bv) {
+    case 32: return run_fold_fast<KDA, ST, 32, MAT>(a, lay, s);
+    case 64: return run_fold_fast<KDA, ST, 64, MAT>(a, lay, s);
+    case 128: return run_fold_fast<KDA, ST, 128, MAT>(a, lay, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool KDA, typename ST>
+static hipError_t fold_fast_mat(int bv, bool mat, const FoldArgs& a, const FoldFastLayout& lay,
+                                hipStream_t s) {
+  return mat ? fold_fast_bv<KDA, ST, true>(bv, a, lay, s)
+             : fold_fast_bv<KDA, ST, false>(bv, a, lay, s);
+}
+
+hipError_t launch_fold_fast(bool kda, int state_bf16, int bv, bool materialize,
+                            const FoldArgs& a, const FoldFastLayout& lay, hipStream_t s) {
+  if (kda) return state_bf16 ? fold_fast_mat<true, bf16>(bv, materialize, a, lay, s)
+                             : fold_fast_mat<true, float>(bv, materialize, a, lay, s);
+  return state_bf16 ? fold_fast_mat<false, bf16>(bv, materialize, a, lay, s)
+                    : fold_fast_mat<false, float>(bv, materialize, a, lay, s);
+}
+
+}  // namespace rs

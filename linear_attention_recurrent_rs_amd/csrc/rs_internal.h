@@ -167,13 +167,38 @@ inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
   return l;
 }
 
-// Launchers (defined in rs_kernels.hip and rs_verify_fast.hip).  Return hipGetLastError() after the launch.
+// LDS plan of the dk = 128 commit fold / materialize (rs_fold_fast.hip).  Byte offsets.
+struct FoldFastLayout {
+  int hkeys;    // history keys, bf16 [L x kKeyStride]               (HBM -> LDS copy)
+  int hd;       // history deltas of this tile, fp32 [L x bv]       (HBM -> LDS copy)
+  int hg;       // gates, fp32 [L] (GDN) or [L x 128] (KDA; then the decayed keys)
+  int gam_i;    // GDN: suffix decay of each record [L]
+  int Gam;      // KDA: total decay per key channel [128]
+  int total;
+};
+
+inline FoldFastLayout fold_fast_layout(bool kda, int bv, int L) {
+  auto al = [](int x) { return (x + 15) & ~15; };
+  FoldFastLayout l{};
+  int o = 0;
+  l.hkeys = o; o += al(L * kKeyStride * 2);
+  l.hd = o; o += al(L * bv * 4);
+  l.hg = o; o += al(kda ? L * 128 * 4 : L * 4);
+  l.gam_i = o; o += kda ? 0 : al(L * 4);
+  l.Gam = o; o += kda ? al(128 * 4) : 0;
+  l.total = o;
+  return l;
+}
+
+// Launchers (defined in rs_kernels.hip, rs_verify_fast.hip and rs_fold_fast.hip).  Return hipGetLastError() after the launch.
 hipError_t launch_verify(bool kda, int act_bf16, int state_bf16, int bv, int tmax,
                          const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_fast(bool kda, int state_bf16, int bv, int tmax, const VerifyArgs& a,
                               const FastLayout& lay, hipStream_t s);
 hipError_t launch_fold(bool kda, int act_bf16, int state_bf16, int bv, bool materialize,
                        const FoldArgs& a, hipStream_t s);
+hipError_t launch_fold_fast(bool kda, int state_bf16, int bv, bool materialize,
+                            const FoldArgs& a, const FoldFastLayout& lay, hipStream_t s);
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
 
 }  // namespace rs
