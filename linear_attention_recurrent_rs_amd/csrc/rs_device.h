@@ -105,6 +105,27 @@ struct Tile {
   }
 };
 
+// ------------------------------------------------------------------ lane sums
+// v[l] + v[l ^ m] for m = 8, 16, 32 without the LDS pipe.  gfx950's permlane swaps trade
+// rows (16 lanes) between two registers: with both operands v, permlane16_swap returns
+// (rows 0,0,2,2 ; rows 1,1,3,3) and permlane32_swap (rows 0,1,0,1 ; rows 2,3,2,3), whose
+// sums are the xor-16 and xor-32 partner sums.  Within a row, rotating by 8 reaches l ^ 8.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <int M>
+__device__ __forceinline__ float xor_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  if constexpr (M == 8) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, int(u), 0x128, 0xF, 0xF, false));
+  } else if constexpr (M == 16) {
+    const u32x2 p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    static_assert(M == 32, "partner distance 8, 16 or 32");
+    const u32x2 p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+}
+
 // ------------------------------------------------------------------ grid order
 // Hardware hands workgroup p to XCD p % 8.  Return a logical index so that each XCD
 // receives one contiguous range of logical indices (neighbouring value heads of one

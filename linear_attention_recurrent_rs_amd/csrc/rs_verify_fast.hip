@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   constexpr int NV2 = 2 * TMAX;
   constexpr int VPP = (NV2 < 8) ? NV2 : 8;           // readout vectors per pass
   constexpr int NPASS = NV2 / VPP;
-  static_assert(QPT >= 1 && DK % (4 * RG) == 0 && CC <= 64, "tile split");
+  static_assert(QPT >= 1 && DK % (4 * RG) == 0 && CC >= 8 && CC <= 32, "tile split");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -425,12 +425,16 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
         acc[mm] += s[j][3] * x[3];
       }
     }
+    // row groups of a wave sit CC lanes apart: sum partners at CC, 2 CC, ... < 64
 #pragma unroll
-    for (int off = CC; off < 64; off <<= 1) {
+    for (int mm = 0; mm < VPP; ++mm) {
 #pragma unroll
-      for (int mm = 0; mm < VPP; ++mm) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[mm][jj] += __shfl_xor(acc[mm][jj], off);
+      for (int jj = 0; jj < 4; ++jj) {
+        float v = acc[mm][jj];
+        if constexpr (CC <= 8) v = xor_sum<8>(v);
+        if constexpr (CC <= 16) v = xor_sum<16>(v);
+        v = xor_sum<32>(v);
+        acc[mm][jj] = v;
       }
     }
     if (lane < CC) {
