@@ -58,10 +58,11 @@ rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
   rs_status st = check_common(d, true);
   if (st != RS_OK) return st;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
-  p->tmax = tmax_of(d->T);
   p->bv = choose_bv(d);
   for (;;) {
     p->fast = use_fast(d, p->bv);
+    // the fast verify is compiled for every window up to 4 and for 8 and 16 beyond
+    p->tmax = (p->fast && d->T <= 4) ? d->T : tmax_of(d->T);
     if (p->fast) p->flay = rs::fast_layout(kda, p->bv, p->tmax, d->T, d->ring_cap);
     else p->lay = rs::verify_layout(kda, dbytes(d->state_dtype), p->bv, p->tmax, d->T, d->dk,
                                     d->ring_cap);

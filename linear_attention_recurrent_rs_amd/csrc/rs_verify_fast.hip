@@ -527,6 +527,7 @@ static hipError_t fast_tmax(int tmax, const VerifyArgs& a, const FastLayout& lay
   switch (tmax) {
     case 1: return run_fast<KDA, ST, BV, 1>(a, lay, s);
     case 2: return run_fast<KDA, ST, BV, 2>(a, lay, s);
+    case 3: return run_fast<KDA, ST, BV, 3>(a, lay, s);
     case 4: return run_fast<KDA, ST, BV, 4>(a, lay, s);
     case 8: return run_fast<KDA, ST, BV, 8>(a, lay, s);
     case 16: return run_fast<KDA, ST, BV, 16>(a, lay, s);
