@@ -59,6 +59,10 @@ rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
   if (st != RS_OK) return st;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
   p->bv = choose_bv(d);
+  // a bf16 state tile of 64 columns is only 16 KB: the fast verify takes whole 128-column
+  // rows then, so that a workgroup moves as many bytes as an fp32 tile of 64 columns
+  if (d->tile_v == 0 && d->state_dtype == RS_BF16 && d->dv % 128 == 0 && use_fast(d, 128))
+    p->bv = 128;
   for (;;) {
     p->fast = use_fast(d, p->bv);
     // the fast verify is compiled for every window up to 4 and for 8 and 16 beyond

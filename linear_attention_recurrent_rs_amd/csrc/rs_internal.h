@@ -128,7 +128,9 @@ struct FastLayout {
   int xs;       // KDA: window vectors times the in-window prefix decay [2*tmax x xs_stride]
   int xr;       // readout vectors, q_t and k_t interleaved [nvec_pad x xs_stride]
   int C;        // history scores [lp x cs] (GDN: undecayed) or 4 partial sums of them (KDA)
-  int red;      // per-wave readout partial sums [4 x nvec_pad x bv]
+  int red;      // per-wave readout partial sums [4 x vpp x bv]; all vectors on the MFMA
+                //   readout (bv 64, tmax >= 8): [4 x nvec_pad x bv]
+  int hist;     // history part of the readout [nvec_pad x bv]
   int Am, Qm;   // window pair scalars [tmax x tmax]
   int total;
   int xs_stride;
@@ -160,7 +162,9 @@ inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
   l.xs = o; o += kda ? al(2 * tmax * l.xs_stride * 4) : 0;
   l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
   l.C = o; o += al((kda ? 4 : 1) * l.lp * l.cs * 4);
-  l.red = o; o += al(4 * l.nvec_pad * bv * 4);
+  // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readout)
+  l.red = o; o += al(4 * ((bv == 64 && tmax >= 8) ? l.nvec_pad : vpp) * bv * 4);
+  l.hist = o; o += al(l.nvec_pad * bv * 4);
   l.Am = o; o += al(tmax * tmax * 4);
   l.Qm = o; o += al(tmax * tmax * 4);
   l.total = o;

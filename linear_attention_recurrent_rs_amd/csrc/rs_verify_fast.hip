@@ -103,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   float* xr = reinterpret_cast<float*>(smem + lay.xr);
   float* Cs = reinterpret_cast<float*>(smem + lay.C);
   float* red = reinterpret_cast<float*>(smem + lay.red);
+  float* hist = reinterpret_cast<float*>(smem + lay.hist);
   float* Am = reinterpret_cast<float*>(smem + lay.Am);
   float* Qm = reinterpret_cast<float*>(smem + lay.Qm);
 
@@ -189,11 +190,25 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
         }
       }
       for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
-    } else {
-      for (int i = tid - DK; i < nh; i += kThreads - DK) {
-        float g = 1.f;
-        for (int j = i + 1; j < nh; ++j) g *= hg[j];
-        gam_i[i] = g;
+    } else if (wave == 2) {
+      // gamma_i = prod_{i<j<nh} alpha_j: an inclusive suffix product over the lanes of
+      // one wave, shifted by one lane (rings up to 64 records; longer rings loop)
+      if (L <= 64) {
+        float v = lane < nh ? hg[lane] : 1.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float o = __shfl_down(v, off);
+          if (lane + off < 64) v *= o;
+        }
+        float ex = __shfl_down(v, 1);
+        if (lane == 63) ex = 1.f;
+        if (lane < nh) gam_i[lane] = ex;
+      } else {
+        for (int i = lane; i < nh; i += 64) {
+          float g = 1.f;
+          for (int j = i + 1; j < nh; ++j) g *= hg[j];
+          gam_i[i] = g;
+        }
       }
     }
   } else {
@@ -322,41 +337,41 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   }
   lds_barrier();
 
-  // 6. history part of the readout, before the tile is touched: wave w sums
-  // d_i[c] C[i][m] over the records i = w, w + 4, ... into its partial red[w][m][c]
-  // (vectors in readout order), to which step 8 adds the wave's tile part
+  // 6. history part of the readout, before the tile is touched:
+  //   hist[m][c] = sum_i d_i[c] w_i[m],  w_i[m] = gamma_i G_t(m) (k_i . x_m)  (GDN; KDA: the
+  //   summed partial scores), vectors m in readout order.  An MFMA contraction over the
+  //   records: A = d_i of 16 columns, B = w_i of 16 vectors, four records per step; wave w
+  //   takes the column blocks w, w + 4, ...
   const int NP = lay.nvec_pad;
   if (hrows > 0) {
-    for (int c = lane; c < BV; c += 64) {
-      float hP[NV2];
+    constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
-      for (int m = 0; m < NV2; ++m) hP[m] = 0.f;
-      for (int i = wave; i < hrows; i += kWaves) {
-        const float di = hd[i * BV + c];
-        const float w = KDA ? di : di * gam_i[i];
-#pragma unroll
-        for (int m = 0; m < NV2; ++m) {
-          if (m < nvec) {
-            const int t = m >> 1, col = (m & 1) ? T + t : t;   // score column of vector m
-            float cm = Cs[i * CS + col];
-            if (KDA) {
-              const int plane = lay.lp * CS;
-              cm = (cm + Cs[plane + i * CS + col]) +
-                   (Cs[2 * plane + i * CS + col] + Cs[3 * plane + i * CS + col]);
-            }
-            hP[m] = fmaf(w, cm, hP[m]);
+    for (int vb = 0; vb < NVB; ++vb) {
+      const int mv = vb * 16 + l16;                        // this lane's vector (B column)
+      const bool mok = mv < nvec;
+      const int tv = mv >> 1, colm = (mv & 1) ? T + tv : tv;
+      const float Gm = KDA ? 1.f : gate_product(gate_s, -1, tv);
+      for (int cb = wave; cb < NCB; cb += kWaves) {
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < (hrows + 3) >> 2; ++ks) {
+          const int rec = 4 * ks + g4;
+          const bool ok = rec < hrows;
+          const int rs = ok ? rec : 0;                     // a row that exists; selected away
+          const float dv_ = hd[rs * BV + cb * 16 + l16];
+          float w;
+          if (KDA) {
+            const int plane = lay.lp * CS, o = rs * CS + (mok ? colm : 0);
+            w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
+          } else {
+            w = (Cs[rs * CS + (mok ? colm : 0)] * gam_i[rs]) * Gm;
           }
+          acc = mfma_16x16x4(ok ? dv_ : 0.f, (ok && mok) ? w : 0.f, acc);
         }
+        // lane holds columns cb*16 + 4*g4 + j of vector vb*16 + l16
+        if (mv < NP) store4(hist + mv * BV + cb * 16 + 4 * g4, acc);
       }
-#pragma unroll
-      for (int m = 0; m < NV2; ++m)
-        if (m < nvec) red[(wave * NP + m) * BV + c] = KDA ? hP[m] : hP[m] * Gp[m >> 1];
     }
   }
-
-  // the partials above are read back by other lanes of the same wave in step 8: LDS
-  // operations of a wave complete in order, so only compiler reordering must be ruled out
-  asm volatile("" ::: "memory");
 
   // 7. rows that overflow.  On a fused fold the window's keys and gates go to rows
   // 0..T-1, which other workgroups of the key group may still read: only the last of
@@ -404,63 +419,121 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
     }
   }
 
-  // 8. tile part of the readout, S^T xr_m over this thread's rows, summed over the row
-  // groups of the wave by lane shuffles; one partial per wave goes to LDS
+  // 8. tile part of the readout, S^T xr_m over this thread's rows; each wave's partial
+  // goes to LDS, and the thread of column c gathers P_m = sum of the 4 partials (+ the
+  // history part) into registers.
+  float Pv[NV2];
 #pragma unroll
-  for (int ps = 0; ps < NPASS; ++ps) {
-    const int m0 = ps * VPP;
-    if (m0 >= nvec) break;
-    f4 acc[VPP];
+  for (int m = 0; m < NV2; ++m) Pv[m] = 0.f;
+  if constexpr (CC == 16 && TMAX >= 8) {
+    // Many window vectors: an MFMA contraction over the tile rows.  The registers are
+    // already an A operand: lane l holds column 4*(l%16) + jj of the rows of row group
+    // 4*wave + l/16, so for fixed (j, i, jj) A[m][k] = S[row(k)][4m + jj] with K = the
+    // wave's 4 row groups; B[k][n] = xr_n[row(k)].  Lane l ends with P of vector l%16 at
+    // columns 16*(l/16) + 4e + jj (element e of accumulator jj).
+    constexpr int NVB = (NV2 + 15) / 16;
 #pragma unroll
-    for (int mm = 0; mm < VPP; ++mm) acc[mm] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int vb = 0; vb < NVB; ++vb) {
+      if (vb * 16 >= nvec) break;
+      const int n = vb * 16 + l16;
+      const bool nok = n < lay.nvec_pad;
+      const float* xrow = xr + (nok ? n : 0) * XS;
+      f4 D[4];
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int rq = rg + RG * j;
+      for (int jj = 0; jj < 4; ++jj) D[jj] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mm = 0; mm < VPP; ++mm) {
-        const f4 x = load4(xr + (m0 + mm) * XS + 4 * rq);
-        acc[mm] += s[j][0] * x[0];
-        acc[mm] += s[j][1] * x[1];
-        acc[mm] += s[j][2] * x[2];
-        acc[mm] += s[j][3] * x[3];
+      for (int j = 0; j < QPT; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xb = xrow[4 * (rg + RG * j) + i];
+          const float b = nok ? xb : 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) D[jj] = mfma_16x16x4(s[j][i][jj], b, D[jj]);
+        }
+      }
+      if (nok) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          store4(red + (wave * lay.nvec_pad + n) * BV + 16 * g4 + 4 * e,
+                 f4{D[0][e], D[1][e], D[2][e], D[3][e]});
       }
     }
-    // row groups of a wave sit CC lanes apart: sum partners at CC, 2 CC, ... < 64
+    lds_barrier();
+    if (tid < BV) {
+      const int NPd = lay.nvec_pad;
 #pragma unroll
-    for (int mm = 0; mm < VPP; ++mm) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float v = acc[mm][jj];
-        if constexpr (CC <= 8) v = xor_sum<8>(v);
-        if constexpr (CC <= 16) v = xor_sum<16>(v);
-        v = xor_sum<32>(v);
-        acc[mm][jj] = v;
+      for (int m = 0; m < NV2; ++m) {
+        if (m < nvec) {
+          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
+                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
+          if (hrows > 0) p += hist[m * BV + tid];
+          Pv[m] = p;
+        }
       }
     }
-    if (lane < CC) {
-      // this wave's history partial for these columns was written by lanes of this same
-      // wave, earlier in program order
+  } else {
+    // Few window vectors: FMAs over this thread's rows, then lane sums across the row
+    // groups of the wave, one pass of VPP vectors at a time.
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+      const int m0 = ps * VPP;
+      if (m0 >= nvec) break;
+      if (ps > 0) lds_barrier();                   // the previous pass's partials are read
+      f4 acc[VPP];
+#pragma unroll
+      for (int mm = 0; mm < VPP; ++mm) acc[mm] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < QPT; ++j) {
+        const int rq = rg + RG * j;
+#pragma unroll
+        for (int mm = 0; mm < VPP; ++mm) {
+          const f4 x = load4(xr + (m0 + mm) * XS + 4 * rq);
+          acc[mm] += s[j][0] * x[0];
+          acc[mm] += s[j][1] * x[1];
+          acc[mm] += s[j][2] * x[2];
+          acc[mm] += s[j][3] * x[3];
+        }
+      }
+      // row groups of a wave sit CC lanes apart: sum partners at CC, 2 CC, ... < 64
 #pragma unroll
       for (int mm = 0; mm < VPP; ++mm) {
-        float* r = red + (wave * NP + m0 + mm) * BV + 4 * cc;
-        store4(r, (hrows > 0 && m0 + mm < nvec) ? acc[mm] + load4(r) : acc[mm]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float v = acc[mm][jj];
+          if constexpr (CC <= 8) v = xor_sum<8>(v);
+          if constexpr (CC <= 16) v = xor_sum<16>(v);
+          v = xor_sum<32>(v);
+          acc[mm][jj] = v;
+        }
+      }
+      if (lane < CC) {
+#pragma unroll
+        for (int mm = 0; mm < VPP; ++mm) store4(red + (wave * VPP + mm) * BV + 4 * cc, acc[mm]);
+      }
+      lds_barrier();
+      if (tid < BV) {
+#pragma unroll
+        for (int mm = 0; mm < VPP; ++mm) {
+          const int m = m0 + mm;
+          if (m < nvec) {
+            float p = (red[mm * BV + tid] + red[(VPP + mm) * BV + tid]) +
+                      (red[(2 * VPP + mm) * BV + tid] + red[(3 * VPP + mm) * BV + tid]);
+            if (hrows > 0) p += hist[m * BV + tid];
+            Pv[m] = p;
+          }
+        }
       }
     }
   }
-  lds_barrier();
 
-  // 9. per column: the readout (sum of the 4 wave partials), forward
-  // substitution over the window, outputs, ring deltas
+  // 9. per column: forward substitution over the window, outputs, ring deltas
   if (tid < BV) {
     const int c = tid, col = col0 + c;
     float d[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        const int m = 2 * t + 1;
-        const float pk = ((red[m * BV + c] + red[(NP + m) * BV + c]) +
-                          (red[(2 * NP + m) * BV + c] + red[(3 * NP + m) * BV + c]));
-        float U = beta_s[t] * (to_f32(xv[t * BV + c]) - pk);
+        float U = beta_s[t] * (to_f32(xv[t * BV + c]) - Pv[2 * t + 1]);
 #pragma unroll
         for (int u = 0; u < t; ++u) U = fmaf(-Am[t * TMAX + u], d[u], U);
         d[t] = U;
@@ -469,9 +542,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       if (t < T) {
-        const int m = 2 * t;
-        float o = ((red[m * BV + c] + red[(NP + m) * BV + c]) +
-                   (red[(2 * NP + m) * BV + c] + red[(3 * NP + m) * BV + c]));
+        float o = Pv[2 * t];
 #pragma unroll
         for (int u = 0; u <= t; ++u) o = fmaf(Qm[t * TMAX + u], d[u], o);
         a.out[((tok0 + t) * hv + h) * dv + col] = o;

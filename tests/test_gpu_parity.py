@@ -104,6 +104,15 @@ def test_key_group_xcd_order(name, cfg):
     _run(cfg)
 
 
+@pytest.mark.parametrize('T,L', [(4, 16), (6, 24), (16, 16)])
+def test_wide_windows(T, L):
+    """fp32 state, 64-column tiles, windows of 4 and more (from 5 on, the readout over the
+    tile runs as an MFMA contraction; T = 16: two blocks of 16 window vectors)."""
+    cfg = W.CONFIGS['c1'].with_(B=6, null_rows=1, hk=2, hv=4, T=T, L=L,
+                                accept=('uniform', 0, T), steps=8, cursor_init='zero')
+    _run(cfg)
+
+
 def test_odd_shapes():
     """dk=dv=16 (one 16-wide tile), dv=48 (three 16-wide tiles), dk=64, ring == window."""
     _run(W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=16, dv=48, L=3, T=3, accept=('uniform', 0, 3),
