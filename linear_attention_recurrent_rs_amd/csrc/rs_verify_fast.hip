@@ -53,6 +53,13 @@ __device__ __forceinline__ float gate_product(const float (&g)[TMAX], int lo, in
   return p;
 }
 
+// A DPP lane move within 16-lane rows; lanes without a source in their row get 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_one(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+
 template <int TMAX>
 __device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
   float r = 0.f;
@@ -173,7 +180,22 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
     }
   }
   if (!KDA) {
-    for (int i = 0; i < nh; ++i) Gam *= hg[i];
+    if (L <= 16) {
+      // Suffix products of the gates within each 16-lane row by DPP (row_shl k: lane i
+      // reads lane i + k of its row; lanes past the row end keep 1): lane i of a row ends
+      // with prod_{i<=j<nh} alpha_j, so lane 0 holds Gam and lane i + 1 gamma_i.
+      const int li = lane & 15;
+      float v = li < nh ? hg[li] : 1.f;
+      v *= dpp_one<0x101>(v);
+      v *= dpp_one<0x102>(v);
+      v *= dpp_one<0x104>(v);
+      v *= dpp_one<0x108>(v);
+      Gam = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+      const float ex = dpp_one<0x101>(v);
+      if (wave == 2 && lane < nh) gam_i[lane] = ex;
+    } else {
+      for (int i = 0; i < nh; ++i) Gam *= hg[i];
+    }
     if (tid < DK) {
       float xq[TMAX], xk[TMAX];
 #pragma unroll
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
         }
       }
       for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
-    } else if (wave == 2) {
+    } else if (wave == 2 && L > 16) {
       // gamma_i = prod_{i<j<nh} alpha_j: an inclusive suffix product over the lanes of
       // one wave, shifted by one lane (rings up to 64 records; longer rings loop)
       if (L <= 64) {
