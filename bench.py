@@ -17,7 +17,7 @@ value = verified tokens per second per layer = live rows * T * layers / step tim
 roofline: the verify kernel; achieved = algorithmic bytes per launch (from the integer
 cursor model: state read, inputs, history records read, outputs and ring writes, the
 state write of rows that fold) / mean launch time from HIP events on the launch stream
-around every verify of the timed steps.  cpu_baseline: the fp64 oracle on a bounded
+around each timed step's back-to-back verifies (divided by the layer count).  cpu_baseline: the fp64 oracle on a bounded
 sample of the same workload, single-threaded.
 
 extra: the T = 3 case; the T = 1 verify at three history states (none, steady, every row
@@ -124,13 +124,15 @@ def run_gpu(T: int, steps: int, warmup: int, layers: int, tile_v: int, n_inputs:
     live = [r for r in range(cfg.B) if slots_np[r] >= 0]
 
     def step(s, events=None):
+        # the layers' verifies run back to back between one pair of events: a pair around
+        # every launch would add the events' own stream synchronisation to each launch
         j = s % n_inputs
+        if events is not None:
+            events[0].record(stream)
         for l in range(layers):
-            if events is not None:
-                events[l][0].record(stream)
             verify_calls[j][l](stream)
-            if events is not None:
-                events[l][1].record(stream)
+        if events is not None:
+            events[1].record(stream)
         advance_calls[j](stream)
 
     for s in range(warmup):
@@ -138,8 +140,7 @@ def run_gpu(T: int, steps: int, warmup: int, layers: int, tile_v: int, n_inputs:
         advance_model(host_cursor, slots_np, accepts[s % n_inputs], T, cfg.L)
     torch.cuda.synchronize()
 
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
-          for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     bytes_per_launch = []
     t0 = time.perf_counter()
     for s in range(steps):
@@ -153,8 +154,7 @@ def run_gpu(T: int, steps: int, warmup: int, layers: int, tile_v: int, n_inputs:
         advance_model(host_cursor, slots_np, accepts[(warmup + s) % n_inputs], T, cfg.L)
     # the device cursors must follow the host model exactly
     assert np.array_equal(cursor.cpu().numpy(), host_cursor), 'cursor model diverged'
-    durs = np.array([[ev[s][l][0].elapsed_time(ev[s][l][1]) for l in range(layers)]
-                     for s in range(steps)])            # ms
+    durs = np.array([ev[s][0].elapsed_time(ev[s][1]) / layers for s in range(steps)])  # ms
     ms_step = (t1 - t0) * 1e3 / steps
     mean_launch_ms = float(durs.mean())
     mean_bytes = float(np.mean(bytes_per_launch))

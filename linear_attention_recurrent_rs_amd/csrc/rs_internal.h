@@ -130,7 +130,7 @@ struct FastLayout {
   int C;        // history scores [lp x cs] (GDN: undecayed) or 4 partial sums of them (KDA)
   int red;      // per-wave readout partial sums [4 x vpp x bv]; all vectors on the MFMA
                 //   readout (bv 64, tmax >= 8): [4 x nvec_pad x bv]
-  int hist;     // history part of the readout [nvec_pad x bv]
+  int hist;     // history part of the readout [nvec_pad x bv] (MFMA readout only)
   int Am, Qm;   // window pair scalars [tmax x tmax]
   int total;
   int xs_stride;
@@ -164,7 +164,7 @@ inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
   l.C = o; o += al((kda ? 4 : 1) * l.lp * l.cs * 4);
   // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readout)
   l.red = o; o += al(4 * ((bv == 64 && tmax >= 8) ? l.nvec_pad : vpp) * bv * 4);
-  l.hist = o; o += al(l.nvec_pad * bv * 4);
+  l.hist = o; o += (bv == 64 && tmax >= 8) ? al(l.nvec_pad * bv * 4) : 0;
   l.Am = o; o += al(tmax * tmax * 4);
   l.Qm = o; o += al(tmax * tmax * 4);
   l.total = o;

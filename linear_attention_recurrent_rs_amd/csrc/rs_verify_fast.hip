@@ -359,13 +359,15 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   }
   lds_barrier();
 
-  // 6. history part of the readout, before the tile is touched:
+  // 6. (many window vectors) history part of the readout, before the tile is touched:
   //   hist[m][c] = sum_i d_i[c] w_i[m],  w_i[m] = gamma_i G_t(m) (k_i . x_m)  (GDN; KDA: the
   //   summed partial scores), vectors m in readout order.  An MFMA contraction over the
   //   records: A = d_i of 16 columns, B = w_i of 16 vectors, four records per step; wave w
-  //   takes the column blocks w, w + 4, ...
+  //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
+  //   the history part, step 8.)
   const int NP = lay.nvec_pad;
-  if (hrows > 0) {
+  constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
+  if (MFMA_READOUT && hrows > 0) {
     constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   float Pv[NV2];
 #pragma unroll
   for (int m = 0; m < NV2; ++m) Pv[m] = 0.f;
-  if constexpr (CC == 16 && TMAX >= 8) {
+  if constexpr (MFMA_READOUT) {
     // Many window vectors: an MFMA contraction over the tile rows.  The registers are
     // already an A operand: lane l holds column 4*(l%16) + jj of the rows of row group
     // 4*wave + l/16, so for fixed (j, i, jj) A[m][k] = S[row(k)][4m + jj] with K = the
@@ -504,6 +506,27 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
       f4 acc[VPP];
 #pragma unroll
       for (int mm = 0; mm < VPP; ++mm) acc[mm] = f4{0.f, 0.f, 0.f, 0.f};
+      // history part first (it needs no tile): row group rg takes records rg, rg + RG, ...
+      // and adds d_i[4 columns] * w_i[m], w_i[m] = gamma_i G_t(m) (k_i . x_m) (KDA: the
+      // summed partial scores); the lane sums below reduce it with the tile part
+      for (int i = rg; i < hrows; i += RG) {
+        const f4 dq = load4(hd + i * BV + 4 * cc);
+        const float gi = KDA ? 1.f : gam_i[i];
+#pragma unroll
+        for (int mm = 0; mm < VPP; ++mm) {
+          const int mv = m0 + mm, t = mv >> 1, col = (mv & 1) ? T + t : t;
+          if (mv < nvec) {
+            float w;
+            if (KDA) {
+              const int plane = lay.lp * CS, o = i * CS + col;
+              w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
+            } else {
+              w = (Cs[i * CS + col] * gi) * Gp[t];
+            }
+            acc[mm] += dq * w;
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
         const int rq = rg + RG * j;
@@ -538,10 +561,8 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
         for (int mm = 0; mm < VPP; ++mm) {
           const int m = m0 + mm;
           if (m < nvec) {
-            float p = (red[mm * BV + tid] + red[(VPP + mm) * BV + tid]) +
-                      (red[(2 * VPP + mm) * BV + tid] + red[(3 * VPP + mm) * BV + tid]);
-            if (hrows > 0) p += hist[m * BV + tid];
-            Pv[m] = p;
+            Pv[m] = (red[mm * BV + tid] + red[(VPP + mm) * BV + tid]) +
+                    (red[(2 * VPP + mm) * BV + tid] + red[(3 * VPP + mm) * BV + tid]);
           }
         }
       }
