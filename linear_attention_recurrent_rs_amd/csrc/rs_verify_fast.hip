@@ -26,6 +26,8 @@
 // its prefix into the registers, writes the state back once and reads out with no
 // history.  Every sum over window positions runs over causal positions only, so values at
 // rejected positions never reach accepted outputs.
+#include <type_traits>
+
 #include "rs_device.h"
 #include "rs_internal.h"
 
@@ -60,6 +62,21 @@ __device__ __forceinline__ float dpp_one(float v) {
                                                     0xF, 0xF, false));
 }
 
+// Sum over groups of N = 2, 4 or 8 adjacent lanes (every lane of a group gets the sum):
+// quad_perm swaps within quads, then the other quad of an 8-lane half row by mirroring.
+template <int N>
+__device__ __forceinline__ float adjacent_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8, "groups of 2, 4 or 8 lanes");
+  auto mv = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      0xF, 0xF, false));
+  };
+  v += mv(v, std::integral_constant<int, 0xB1>{});       // quad_perm 1,0,3,2
+  if constexpr (N >= 4) v += mv(v, std::integral_constant<int, 0x4E>{});   // 2,3,0,1
+  if constexpr (N == 8) v += mv(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  return v;
+}
+
 template <int TMAX>
 __device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
   float r = 0.f;
@@ -84,7 +101,17 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cc = tid % CC, rg = tid / CC;
+  // Lane mapping.  Column quad fastest (cc = lane % CC) makes 16 consecutive lanes read
+  // one whole 256-byte row segment, the best load order; the MFMA readout needs it too
+  // (its A operand).  With 3 or 4 window vectors per pass the FMA readout's row-group
+  // sums dominate instead, so there a wave's RL = 64 / CC row groups sit on adjacent
+  // lanes and sum by DPP quad operations (one load instruction still covers the same 4
+  // row segments).
+  constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
+  constexpr int RL = 64 / CC;                            // row groups per wave
+  constexpr bool ADJ = !MFMA_READOUT && TMAX >= 3;
+  const int cc = ADJ ? lane / RL : tid % CC;
+  const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
   const int vt = lid % a.NV;
   const int h = (lid / a.NV) % a.hv;
@@ -366,7 +393,6 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
   //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
   //   the history part, step 8.)
   const int NP = lay.nvec_pad;
-  constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   if (MFMA_READOUT && hrows > 0) {
     constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
@@ -539,19 +565,24 @@ __global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, Fas
           acc[mm] += s[j][3] * x[3];
         }
       }
-      // row groups of a wave sit CC lanes apart: sum partners at CC, 2 CC, ... < 64
+      // sum the RL row groups of the wave: adjacent lanes by DPP, or lanes CC apart by
+      // permlane swaps
 #pragma unroll
       for (int mm = 0; mm < VPP; ++mm) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           float v = acc[mm][jj];
-          if constexpr (CC <= 8) v = xor_sum<8>(v);
-          if constexpr (CC <= 16) v = xor_sum<16>(v);
-          v = xor_sum<32>(v);
+          if constexpr (ADJ) {
+            v = adjacent_sum<RL>(v);
+          } else {
+            if constexpr (CC <= 8) v = xor_sum<8>(v);
+            if constexpr (CC <= 16) v = xor_sum<16>(v);
+            v = xor_sum<32>(v);
+          }
           acc[mm][jj] = v;
         }
       }
-      if (lane < CC) {
+      if (ADJ ? lane % RL == 0 : lane < CC) {
 #pragma unroll
         for (int mm = 0; mm < VPP; ++mm) store4(red + (wave * VPP + mm) * BV + 4 * cc, acc[mm]);
       }
