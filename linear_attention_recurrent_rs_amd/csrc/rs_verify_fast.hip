@@ -86,8 +86,11 @@ __device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
   return r;
 }
 
+// Five workgroups per CU (at most ~96 VGPRs) where that fits without spills: 64-column
+// tiles and windows up to 3.  More resident workgroups keep more tile bytes in flight.
 template <bool KDA, typename ST, int BV, int TMAX>
-__global__ __launch_bounds__(kThreads) void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
+__global__ __launch_bounds__(kThreads, ((BV <= 64 && TMAX <= 3) ? 5 : 1))
+void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   constexpr int DK = 128, KS = kKeyStride;
   // Tile split: thread (rg, cc) holds rows 4*(rg + RG*j) + i (j < QPT, i < 4) of column
   // quad cc, so that each load instruction of a wave covers whole 256-byte row segments
