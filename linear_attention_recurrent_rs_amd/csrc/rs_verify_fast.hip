@@ -86,10 +86,13 @@ __device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
   return r;
 }
 
-// Five workgroups per CU (at most ~96 VGPRs) where that fits without spills: 64-column
-// tiles and windows up to 3.  More resident workgroups keep more tile bytes in flight.
+// More resident workgroups keep more tile bytes in flight, so the register cap is raised
+// where that fits without spills: five per CU (at most ~96 VGPRs) for 64-column tiles and
+// four per CU (128 VGPRs) for 128-column bf16 tiles, both for windows up to 3.
 template <bool KDA, typename ST, int BV, int TMAX>
-__global__ __launch_bounds__(kThreads, ((BV <= 64 && TMAX <= 3) ? 5 : 1))
+__global__ __launch_bounds__(kThreads, ((BV <= 64 && TMAX <= 3)                           ? 5
+                                        : (BV == 128 && sizeof(ST) == 2 && TMAX <= 3) ? 4
+                                                                                       : 1))
 void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   constexpr int DK = 128, KS = kKeyStride;
   // Tile split: thread (rg, cc) holds rows 4*(rg + RG*j) + i (j < QPT, i < 4) of column
