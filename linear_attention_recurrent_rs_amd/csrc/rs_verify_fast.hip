@@ -86,13 +86,48 @@ __device__ __forceinline__ float pick(const float (&x)[TMAX], int t) {
   return r;
 }
 
-// More resident workgroups keep more tile bytes in flight, so the register cap is raised
-// where that fits without spills: five per CU (at most ~96 VGPRs) for 64-column tiles and
-// four per CU (128 VGPRs) for 128-column bf16 tiles, both for windows up to 3.
+// One arrival at the fold counter of key group (row, kh); returns the count before it.  A
+// per-lane zero the compiler cannot see through keeps the address divergent, so that the
+// atomic is not rewritten into a wave reduction that reads its result back at once.
+__device__ __forceinline__ int arrive(const VerifyArgs& a, int row, int kh) {
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return __hip_atomic_fetch_add(a.group_counter + (size_t)row * a.hk + kh + zero, 1,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A thread's part of a [128 x BV] tile, rows 4 (rg + RG j) + i, columns 4 cc .. 4 cc + 3,
+// written to the tile at so (row stride dv) with non-temporal stores.  The addresses are
+// a uniform row pointer plus one per-thread byte offset: they take one VGPR, and do not
+// keep the 64-bit addresses of the tile loads alive until a fold writes the tile back.
+template <int QPT, int RG, typename ST>
+__device__ __forceinline__ void store_tile(ST* so, const f4 (&s)[QPT][4], int rg, int cc,
+                                           int dv) {
+  const uint32_t voff = (uint32_t)(4 * rg * dv + 4 * cc) * (uint32_t)sizeof(ST);
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      char* rowp = reinterpret_cast<char*>(so + (size_t)(4 * RG * j + i) * dv);
+      store4_nt(reinterpret_cast<ST*>(rowp + voff), s[j][i]);
+    }
+  }
+}
+
+// Workgroups per CU the register cap is set for.  More resident workgroups keep more tile
+// bytes in flight, so the cap is raised where that fits without spills and measures
+// faster: six per CU (at most 80 VGPRs) for 64-column tiles at windows 2-3 (KDA: 2), five
+// (96 VGPRs) for the other 64-column tiles up to window 3, four (128 VGPRs) for
+// 128-column bf16 tiles up to window 3.  (At window 1 six per CU fit too but run slower.)
+constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
+  return (bv <= 64 && (tmax == 2 || (tmax == 3 && !kda))) ? 6
+         : (bv <= 64 && tmax <= 3)                         ? 5
+         : (bv == 128 && bf16_state && tmax <= 3)          ? 4
+                                                           : 1;
+}
+
 template <bool KDA, typename ST, int BV, int TMAX>
-__global__ __launch_bounds__(kThreads, ((BV <= 64 && TMAX <= 3)                           ? 5
-                                        : (BV == 128 && sizeof(ST) == 2 && TMAX <= 3) ? 4
-                                                                                       : 1))
+__global__ __launch_bounds__(kThreads, fast_min_blocks(KDA, BV, TMAX, sizeof(ST) == 2))
 void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   constexpr int DK = 128, KS = kKeyStride;
   // Tile split: thread (rg, cc) holds rows 4*(rg + RG*j) + i (j < QPT, i < 4) of column
@@ -196,6 +231,13 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   }
   code_fence();
   lds_barrier<QPT * 4>();                                // every copy but the tile is in LDS
+  // fp32 state, on a fold: the arrival of this workgroup at its key group's counter (step 7
+  // explains it), now that its reads of the ring are complete, so that the round trip of
+  // the atomic overlaps the scores.  (bf16 state arrives in step 7: the result, read
+  // there, would otherwise hold its readout until the whole tile had landed.)
+  constexpr bool EARLY_ARRIVAL = sizeof(ST) == 4;
+  int arrived = 0;
+  if (EARLY_ARRIVAL && fold && wave == 0 && lane == 0) arrived = arrive(a, row, kh);
 
   const int nvec = 2 * T, hrows = fold ? 0 : nh;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -435,15 +477,25 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   // ordering is at stake, no data passes through the counter: every increment follows
   // its workgroup's completed reads (the copies landed before the first barrier), and the
   // writes follow the return of the last increment, so a relaxed device-scope atomic
-  // suffices.  Wave 0 increments and later writes.  (Its wait for the returned value also
-  // waits for the tile, as vector-memory operations complete in order: hence here.)
-  int last = 0;
-  if (fold && wave == 0) {
-    int old = 0;
+  // suffices.  Wave 0 increments and reads the returned value.
+  bool last = false;
+  if constexpr (EARLY_ARRIVAL) {
+    // fp32 state (arrival issued in step 3): every path first waits for the tile, before
+    // any write.  The readout below is code shared by rows that fold and rows that do not,
+    // and a wait there for tile loads still in flight would, on a fold, also wait for the
+    // state writes issued before it (the counter covers stores too): a full HBM round trip
+    // under load.  An fp32 tile has in practice landed by now.
+    wait_vmem();
+    last = fold && wave == 0 && __shfl(arrived, 0) == a.G * a.NV - 1;
+  } else if (fold && wave == 0) {
+    // bf16 state: a bf16 tile (twice the columns, smaller loads) is still arriving, and its
+    // readout gains more from consuming it load by load; only the fold path waits, for the
+    // returned value, which, vector-memory operations completing in order, also waits for
+    // the tile.
     if (lane == 0)
-      old = __hip_atomic_fetch_add(a.group_counter + (size_t)row * hk + kh, 1,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = __shfl(old, 0) == a.G * a.NV - 1;
+      arrived = __hip_atomic_fetch_add(a.group_counter + (size_t)row * hk + kh, 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = __shfl(arrived, 0) == a.G * a.NV - 1;
   }
   if (fold) {
     // S <- Gam (.) S + sum_i gamma_i k_i d_i^T in the registers, then one write
@@ -465,12 +517,17 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
       }
     }
     ST* so = static_cast<ST*>(a.state) + (((size_t)slot * hv + h) * DK) * dv + col0;
+    if constexpr (EARLY_ARRIVAL) {
+      store_tile<QPT, RG>(so, s, rg, cc, dv);
+    } else {
+      // stored rounded to bf16; the readout below uses the rounded values
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
+      for (int j = 0; j < QPT; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        store4_nt(so + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc), s[j][i]);
-        s[j][i] = round4<ST>(s[j][i]);
+        for (int i = 0; i < 4; ++i) {
+          store4_nt(so + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc), s[j][i]);
+          s[j][i] = round4<ST>(s[j][i]);
+        }
       }
     }
   }
@@ -635,7 +692,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   // the head's tiles)
   if (wave == 0) {
     if (a.write_pos_out && h == 0 && vt == 0 && lane == 0) a.write_pos_out[row] = base;
-    const bool writer = fold ? (last != 0) : (h % a.G == 0 && vt == 0);
+    const bool writer = fold ? last : (h % a.G == 0 && vt == 0);
     if (writer) {
       bf16* rk = static_cast<bf16*>(a.ring_k);
       for (int i = lane; i < T * (DK / 8); i += 64) {           // 16-byte chunks
