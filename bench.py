@@ -294,25 +294,27 @@ def _rand_setup(cfg, layers, seed=1234):
     return st
 
 
-def history_states(iters=60, layers=8):
-    """The decode verify (T = 1) at three history states, cursors held fixed: no history
-    (every write_pos 0), steady (cursor = row mod 16, the benchmark's spread), and every
-    row folding in the verify (cursor = 16).  Kernel time from HIP events on the stream."""
+def history_states(T=1, iters=60, layers=8):
+    """The decode verify at three history states, cursors held fixed: no history (every
+    write_pos 0), steady (cursors staggered over [0, L - T]: row mod (L - T + 1)), and
+    every row folding in the verify (cursor = L).  Kernel time from HIP events on the
+    stream."""
     import torch
     import linear_attention_recurrent_rs_amd as rs
     import workloads as W
-    cfg = W.CONFIGS['c1']
+    cfg = W.CONFIGS['c1'].with_(T=T)
     st = _rand_setup(cfg, layers)
     dev, slots_np = st['dev'], st['slots_np']
     live = [r for r in range(cfg.B) if slots_np[r] >= 0]
-    out = torch.empty(cfg.B, cfg.hv, cfg.dv, device=dev)
+    out = torch.empty(cfg.B * T, cfg.hv, cfg.dv, device=dev)
     counter = torch.zeros(cfg.B * cfg.hk, dtype=torch.int32, device=dev)
     ins = st['inputs']()
     res = {}
     for name in ('no_history', 'steady', 'all_fold'):
         cur = np.zeros(cfg.num_slots, np.int32)
         for r in live:
-            cur[slots_np[r]] = 0 if name == 'no_history' else (r % cfg.L if name == 'steady' else cfg.L)
+            cur[slots_np[r]] = (0 if name == 'no_history' else
+                                r % (cfg.L - T + 1) if name == 'steady' else cfg.L)
         cursor = torch.from_numpy(cur).to(dev)
         calls = [rs.prepare_verify(False, st['d'], *ins, st['S'][l], st['rk'][l], st['rd'][l],
                                    st['rg'][l], cursor, st['slots'], out, None, counter)
@@ -328,10 +330,33 @@ def history_states(iters=60, layers=8):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / iters * 1e3
         n = [int(cur[slots_np[r]]) for r in live]
-        byts = verify_bytes(cfg, n, [x + 1 > cfg.L for x in n])
+        byts = verify_bytes(cfg, n, [x + T > cfg.L for x in n])
         res[name] = {'kernel_us': round(us, 3), 'achieved_gbs': round(byts / us / 1e3, 1),
                      'frac': round(byts / us / 1e3 / HBM_PEAK_GBS, 4), 'bytes_per_launch': byts}
     return res
+
+
+def stream_reference(nbytes, pools=8, iters=48):
+    """Read rate of the library's plain streaming-read kernel (the verify's load
+    instructions and workgroup size, nothing else) over buffers of the verify's size,
+    rotating over `pools` buffers like the layer pools.  GB/s from HIP events."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    n = (int(nbytes) + 15) // 16 * 4                  # float32 elements, whole 16-byte words
+    bufs = [torch.zeros(n, dtype=torch.float32, device='cuda:0') for _ in range(pools)]
+    sink = torch.zeros(256, dtype=torch.float32, device='cuda:0')
+    stream = torch.cuda.current_stream()
+    for i in range(2 * pools):
+        rs.stream_read(bufs[i % pools], sink, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        rs.stream_read(bufs[i % pools], sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    del bufs
+    return {'bytes': n * 4, 'us': round(us, 3), 'gbs': round(n * 4 / us / 1e3, 1)}
 
 
 def run_workload(name, steps=30, warmup=10):
@@ -485,8 +510,15 @@ def main():
                           'frac': round(r['achieved_gbs'] / HBM_PEAK_GBS, 4),
                           'bytes_per_launch': int(r['bytes_per_launch'])}
     if not args.no_extra:
-        extra['history_states_T1'] = history_states()
-        print(f'# history states: {extra["history_states_T1"]}', file=sys.stderr, flush=True)
+        ref = stream_reference(p['bytes_per_launch'])
+        line['roofline']['stream_read_gbs'] = ref['gbs']
+        line['roofline']['frac_of_stream_read'] = round(p['achieved_gbs'] / ref['gbs'], 4)
+        print(f'# plain streaming read of {ref["bytes"]} B: {ref["us"]} us, {ref["gbs"]} GB/s',
+              file=sys.stderr, flush=True)
+        for T in (1, 3):
+            extra[f'history_states_T{T}'] = history_states(T)
+            print(f'# history states T={T}: {extra[f"history_states_T{T}"]}', file=sys.stderr,
+                  flush=True)
         for name in ('c2', 'c3', 'c4'):
             extra[name] = run_workload(name)
             print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)

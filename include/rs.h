@@ -179,6 +179,17 @@ const char* rs_status_str(rs_status status);
 rs_status rs_verify_launch_info(const rs_dims* dims, int is_kda, int32_t* tile_v,
                                 int32_t* workgroups, int32_t* lds_bytes);
 
+/* Measurement aid, not part of the method: the read-bandwidth reference the verify is
+ * compared with.  Streams `bytes` bytes of src with the load instructions and workgroup
+ * size the verify uses for its state tiles (non-temporal 16-byte vector loads, 256
+ * threads, 16 KiB per workgroup) and does nothing else.
+ *   src   device memory, 16-byte aligned, bytes > 0 and a multiple of 16; only read.
+ *   sink  device memory of 256 floats that the kernel may write (contents unspecified),
+ *         so that the loads are kept.
+ * Enqueued on stream; no synchronisation.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE (size or alignment), RS_E_LAUNCH. */
+rs_status rs_stream_read(const void* src, uint64_t bytes, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'commit_fold',
-           'materialize', 'verify_launch_info', 'library_path', 'F32', 'BF16',
+           'materialize', 'verify_launch_info', 'stream_read', 'library_path', 'F32', 'BF16',
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
            'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE']
 
@@ -72,6 +72,8 @@ def _lib():
         lib.rs_status_str.restype = ctypes.c_char_p
         lib.rs_verify_launch_info.argtypes = [dp, ctypes.c_int, _P, _P, _P]
         lib.rs_verify_launch_info.restype = ctypes.c_int
+        lib.rs_stream_read.argtypes = [_P, ctypes.c_uint64, _P, _P]
+        lib.rs_stream_read.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -197,6 +199,17 @@ def verify_launch_info(d: Dims, kda: bool = False):
                                         ctypes.byref(wg), ctypes.byref(lds)),
            'rs_verify_launch_info')
     return tv.value, wg.value, lds.value
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement aid: stream all of src (a contiguous GPU tensor) with the verify's load
+    instructions; sink is a float32 GPU tensor of 256 elements the kernel may write."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError('src must be a contiguous GPU tensor')
+    nbytes = src.numel() * src.element_size()
+    _check(_lib().rs_stream_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_uint64(nbytes),
+                                 _ptr(sink, 'sink', 256, torch.float32), _stream(stream)),
+           'rs_stream_read')
 
 
 # ----------------------------------------------------------------------------- prepared calls

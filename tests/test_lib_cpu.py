@@ -78,3 +78,14 @@ def test_advance_and_fold_validation():
     assert lib.rs_commit_fold(ctypes.byref(d), 0, *([None] * 6), None) == 1
     assert lib.rs_commit_fold(ctypes.byref(d), 1, *([None] * 6), None) == 2
     assert lib.rs_materialize(ctypes.byref(d), 0, *([None] * 7), None) == 1
+
+
+def test_stream_read_validation():
+    """The bandwidth reference rejects bad arguments on the host, before any launch."""
+    lib = rs._lib()
+    fake = ctypes.c_void_p(0x10000)                  # never dereferenced: rejected first
+    assert lib.rs_stream_read(None, 1024, fake, None) == 1
+    assert lib.rs_stream_read(fake, 1024, None, None) == 1
+    assert lib.rs_stream_read(fake, 0, fake, None) == 2
+    assert lib.rs_stream_read(fake, 1000, fake, None) == 2             # not a multiple of 16
+    assert lib.rs_stream_read(ctypes.c_void_p(0x10008), 1024, fake, None) == 2   # misaligned
