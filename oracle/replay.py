@@ -20,6 +20,11 @@ Method (the three pages, read together):
     the draft length; LightLLM force_compress).
   * Rows whose state slot is negative are skipped by every kernel (sglang commit 1).
 
+Ragged windows (LightLLM commit: decode reads every request's window from cumulative
+sequence lengths, q, k, v laid out [tokens, heads, dim]; sglang Modifications: per-request
+verify lengths packed into one token list).  Row r may verify T_r <= T draft tokens; every
+per-row rule below then reads the row's own T_r, and T_r = 0 leaves the row as it is.
+
 Readings where the pages are silent (each listed in the design notes):
   * cursor n, window T, capacity L:  fold_now = n + T > L;  write_pos = 0 if fold_now else n.
   * advance: m = write_pos + accept; fold_len = policy(m); cursor = 0 if fold_len else m.
@@ -54,6 +59,11 @@ def lazy_fold(m: int, next_T: int, L: int) -> bool:
     return m + next_T > L
 
 
+def window(T: int, lens, r: int) -> int:
+    """Window width of row r: the batch's T, or lens[r] when windows are ragged."""
+    return T if lens is None else int(lens[r])
+
+
 def _rows(slots, rows: Optional[Iterable[int]]):
     rr = range(len(slots)) if rows is None else rows
     return [r for r in rr if slots[r] >= 0]
@@ -86,11 +96,13 @@ class ReplayLayer:
         return self._fold_prefix(self.S[s], s, n)
 
 
-def verify(layer: ReplayLayer, cursor, slots, inp, rows=None):
+def verify(layer: ReplayLayer, cursor, slots, inp, rows=None, lens=None):
     """Verify of one layer.  ``inp`` has q, k [B,T,hk,dk], v [B,T,hv,dv], beta [B,T,hv],
-    gate [B,T,hv] or [B,T,hv,dk].  Returns (out [B,T,hv,dv] with NaN for rows not
-    processed, write_pos [B] with -1 for rows not processed).  The cursor is read only."""
-    B, T = inp.v.shape[:2]
+    gate [B,T,hv] or [B,T,hv,dk].  With ``lens`` (ragged windows) row r verifies its
+    first lens[r] <= T tokens.  Returns (out [B,T,hv,dv] with NaN for rows and positions
+    not processed, write_pos [B] with -1 for rows not processed).  The cursor is read
+    only."""
+    B, Tb = inp.v.shape[:2]
     L, G, kda = layer.L, layer.G, layer.kda
     out = np.full(inp.v.shape, np.nan)
     write_pos = np.full(B, -1, dtype=np.int32)
@@ -99,6 +111,7 @@ def verify(layer: ReplayLayer, cursor, slots, inp, rows=None):
         if s not in layer.S:
             continue
         n = int(cursor[s])
+        T = window(Tb, lens, r)
         if fold_now(n, T, L):               # the window would overflow: fold first
             layer.S[s] = layer._fold_prefix(layer.S[s], s, n)
             layer.fused_folds += 1
@@ -119,10 +132,11 @@ def verify(layer: ReplayLayer, cursor, slots, inp, rows=None):
 
 
 def cursor_advance(cursor, fold_len, slots, accept, T: int, L: int, policy: int,
-                   next_T: int = 0, force_mask=None):
+                   next_T: int = 0, force_mask=None, lens=None):
     """Advance the shared cursor once per step, after every layer's verify (in place).
 
-    write_pos is recomputed from the unchanged cursor exactly as verify derived it.
+    write_pos is recomputed from the unchanged cursor exactly as verify derived it (with
+    the row's own window width when ``lens`` gives ragged windows).
     fold_len[s] = m under EVERY_COMMIT, under LAZY when m + next_T > L, under FORCE for
     rows in force_mask (all rows when None), else 0.  Null rows touch nothing."""
     for r in range(len(slots)):
@@ -130,7 +144,7 @@ def cursor_advance(cursor, fold_len, slots, accept, T: int, L: int, policy: int,
         if s < 0:
             continue
         n = int(cursor[s])
-        base = 0 if fold_now(n, T, L) else n
+        base = 0 if fold_now(n, window(T, lens, r), L) else n
         m = base + int(accept[r])
         if policy == FOLD_NONE:
             fl = 0
@@ -184,8 +198,8 @@ class TokenStream:
         return cls({s: layer.committed_state(s, int(cursor[s])) for s in layer.S},
                    layer.kda, layer.G)
 
-    def verify(self, slots, inp, rows=None):
-        B, T = inp.v.shape[:2]
+    def verify(self, slots, inp, rows=None, lens=None):
+        B, Tb = inp.v.shape[:2]
         out = np.full(inp.v.shape, np.nan)
         dels = np.full(inp.v.shape, np.nan)
         self._window = {}
@@ -197,7 +211,7 @@ class TokenStream:
             ks = expand_heads(inp.k[r], self.G)
             qs = expand_heads(inp.q[r], self.G)
             states = []
-            for t in range(T):
+            for t in range(window(Tb, lens, r)):
                 H, d = token_update(H, ks[t], inp.v[r, t], inp.beta[r, t], inp.gate[r, t],
                                     self.kda)
                 out[r, t] = readout(H, qs[t])

@@ -76,10 +76,10 @@ def _layer(S0, L, hk, hv, dk, dv, kda, cursor=None, rng=None):
 
 
 def run_both(S0, steps_inputs, accepts, slots, L, T, hk, hv, kda, policies,
-             cursor0=None, ring_rng=None, force_masks=None):
-    """Run the replay state machine and the token-stream definition side by side.
-    Returns (max relative output gap, max relative committed-state gap, fused folds,
-    cursor trace)."""
+             cursor0=None, ring_rng=None, force_masks=None, lens=None):
+    """Run the replay state machine and the token-stream definition side by side
+    (``lens``: per-step ragged window widths, or None).  Returns (max relative output
+    gap, max relative committed-state gap, fused folds, cursor trace)."""
     nslots = S0.shape[0]
     dk, dv = S0.shape[2], S0.shape[3]
     cursor = np.zeros(nslots, np.int32) if cursor0 is None else cursor0.copy()
@@ -90,13 +90,17 @@ def run_both(S0, steps_inputs, accepts, slots, L, T, hk, hv, kda, policies,
     gap_o = gap_s = 0.0
     trace = []
     for j, (inp, acc) in enumerate(zip(steps_inputs, accepts)):
-        o_rep, wp = rp.verify(layer, cursor, slots, inp)
-        o_def, _ = ts.verify(slots, inp)
+        ln = None if lens is None else lens[j]
+        o_rep, wp = rp.verify(layer, cursor, slots, inp, lens=ln)
+        o_def, _ = ts.verify(slots, inp, lens=ln)
         live = slots >= 0
-        gap_o = max(gap_o, _rel(o_rep[live], o_def[live]))
+        fin = np.isfinite(o_def[live])
+        assert np.array_equal(fin, np.isfinite(o_rep[live])), 'processed positions differ'
+        if fin.any():
+            gap_o = max(gap_o, _rel(o_rep[live][fin], o_def[live][fin]))
         pol, next_T = policies[j]
         fm = None if force_masks is None else force_masks[j]
-        rp.cursor_advance(cursor, fold_len, slots, acc, T, L, pol, next_T, fm)
+        rp.cursor_advance(cursor, fold_len, slots, acc, T, L, pol, next_T, fm, lens=ln)
         rp.commit_fold(layer, fold_len, slots)
         ts.accept(slots, acc)
         trace.append(cursor.copy())
@@ -386,6 +390,82 @@ def pin_nan_isolation():
             assert np.all(np.isfinite(layer.rd[s][:cursor[s]]))
 
 
+def pin_ragged_replay_equals_sequential():
+    """Ragged windows (row r verifies T_r <= T tokens, T_r = 0 included): the replay state
+    machine equals the token-stream definition every step, with staggered cursors,
+    history, fused and commit folds and null rows (fp64, 1e-12)."""
+    rng = np.random.default_rng(22)
+    for kda, T, L, pol in ((False, 4, 6, rp.FOLD_NONE), (False, 3, 5, rp.FOLD_LAZY),
+                           (True, 4, 7, rp.FOLD_NONE), (False, 4, 8, rp.FOLD_EVERY_COMMIT),
+                           (True, 3, 4, rp.FOLD_FORCE)):
+        hk, hv, dk, dv, B, steps = 2, 4, 5, 6, 5, 10
+        nslots = B + 2
+        S0 = rng.standard_normal((nslots, hv, dk, dv)) * 0.3
+        slots = np.array([3, -1, 0, 6, 2], np.int32)
+        cursor0 = np.zeros(nslots, np.int32)
+        for s in (3, 0, 6, 2):
+            cursor0[s] = int(rng.integers(0, L + 1))
+        ins = [_inputs(B, T, hk, hv, dk, dv, kda, rng) for _ in range(steps)]
+        lens = [rng.integers(0, T + 1, size=B).astype(np.int32) for _ in range(steps)]
+        accs = [np.array([rng.integers(0, l + 1) for l in ln], np.int32) for ln in lens]
+        fms = [rng.integers(0, 2, size=B).astype(np.uint8) for _ in range(steps)]
+        go, gs, nf, _ = run_both(S0, ins, accs, slots, L, T, hk, hv, kda,
+                                 [(pol, T)] * steps, cursor0, rng, fms, lens)
+        assert go < 1e-12 and gs < 1e-12, ('ragged replay vs sequential', kda, T, L, pol, go, gs)
+
+
+def pin_ragged_cursor_bruteforce():
+    """Every sequence of (window width, accept length) pairs over 4 steps with T = 2,
+    L = 3 (6^4 = 1296), fused-only and lazy policies: each row's own width decides its
+    overflow (write_pos = 0 exactly when cursor + T_r > L), the window always fits the
+    ring, a width-0 window changes nothing, committed keys sit at ring rows [0, cursor)
+    in accept order, and outputs and the final state equal the definition's."""
+    T, L, steps = 2, 3, 4
+    hk = hv = 1
+    dk = dv = 2
+    rng = np.random.default_rng(23)
+    S0 = rng.standard_normal((1, hv, dk, dv))
+    ins = [_inputs(1, T, hk, hv, dk, dv, False, rng) for _ in range(steps)]
+    slots = np.array([0], np.int32)
+    pairs = [(w, a) for w in range(T + 1) for a in range(w + 1)]
+    for pol in (rp.FOLD_NONE, rp.FOLD_LAZY):
+        for seq in itertools.product(pairs, repeat=steps):
+            layer = _layer(S0, L, hk, hv, dk, dv, False)
+            ts = rp.TokenStream.from_replay(layer, np.zeros(1, np.int32))
+            cursor = np.zeros(1, np.int32)
+            fl = np.zeros(1, np.int32)
+            pending = []
+            for j, (w, a) in enumerate(seq):
+                n = int(cursor[0])
+                ln = np.array([w], np.int32)
+                S_before = layer.S[0].copy()
+                o, wp = rp.verify(layer, cursor, slots, ins[j], lens=ln)
+                o2, _ = ts.verify(slots, ins[j], lens=ln)
+                assert np.all(np.isfinite(o[0, :w])) and np.all(np.isnan(o[0, w:]))
+                if w:
+                    assert _rel(o[0, :w], o2[0, :w]) < 1e-12
+                exp_base = 0 if n + w > L else n
+                assert wp[0] == exp_base and exp_base + w <= L
+                if w == 0:
+                    assert np.array_equal(layer.S[0], S_before)
+                if exp_base == 0:
+                    pending = []
+                acc = np.array([a], np.int32)
+                rp.cursor_advance(cursor, fl, slots, acc, T, L, pol, T, lens=ln)
+                if pol == rp.FOLD_LAZY:
+                    assert (fl[0] > 0) == (exp_base + a + T > L)
+                rp.commit_fold(layer, fl, slots)
+                ts.accept(slots, acc)
+                pending = pending + [ins[j].k[0, t] for t in range(a)]
+                if fl[0]:
+                    pending = []
+                assert 0 <= cursor[0] <= L and cursor[0] == len(pending)
+                for i, key in enumerate(pending):
+                    assert np.array_equal(layer.rk[0][i], key)
+            assert _rel(rp.materialize(layer, cursor, slots)[0], ts.H[0]) < 1e-12
+
+
 ALL_PINS = [pin_exact_rational, pin_exact_grouped_heads, pin_pure_decay, pin_identity_readout,
             pin_write_then_read, pin_grouped_write, pin_replay_equals_sequential,
-            pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation]
+            pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation,
+            pin_ragged_replay_equals_sequential, pin_ragged_cursor_bruteforce]

@@ -67,7 +67,12 @@ def _lazy_late(m, next_T, L):
     return m + next_T > L + 1
 
 
+def _window_ignored(T, lens, r):
+    return T
+
+
 MUTANTS = {
+    'ragged window width ignored': [('window', _window_ignored)],
     'd sign flipped': [('token_update', _tu_sign)],
     'beta dropped from d': [('token_update', _tu_nobeta)],
     'prediction from undecayed state': [('token_update', _tu_pred_undecayed)],
