@@ -132,6 +132,42 @@ rs_status rs_kda_verify(const rs_dims* dims,
                         hipStream_t stream);
 
 /*
+ * rs_gdn_verify_varlen, rs_kda_verify_varlen -- as rs_gdn_verify / rs_kda_verify with
+ * ragged verify windows: each request row verifies its own number of draft tokens, and
+ * the tokens of all rows are packed into one list (LightLLM commit: decode reads every
+ * request window from the cumulative lengths, with q, k, v laid out [tokens, heads, dim];
+ * sglang Modifications: per-request verify lengths packed into one token list).
+ *   cu_seqlens  [B + 1] int32 device memory: row r owns packed tokens
+ *               [cu_seqlens[r], cu_seqlens[r + 1]), its window width T_r; the caller
+ *               keeps cu_seqlens nondecreasing, cu_seqlens[B] <= total_tokens and every
+ *               T_r in [0, dims->T] (dims->T is the widest window of the batch, 1..16).
+ *   total_tokens  rows of the packed inputs and outputs (>= 0)
+ *   q, k        [total_tokens, hk, dk]; v [total_tokens, hv, dv]; beta [total_tokens, hv];
+ *   gate        [total_tokens, hv] (GDN) or [total_tokens, hv, dk] (KDA)
+ *   out         [total_tokens, hv, dv] fp32; packed token j of row r is draft t = j - cu[r]
+ * Every per-row rule reads the row's own T_r: the row folds in-kernel when
+ * cursor + T_r > L, and its records go to ring rows [write_pos, write_pos + T_r).  A row
+ * with T_r = 0 reports write_pos = cursor and reads or writes nothing else.  For memory
+ * safety the kernels clamp out-of-contract lengths to [0, total_tokens] and to dims->T.
+ * Every other argument, and the errors, as for rs_gdn_verify; also RS_E_NULLPTR when
+ * cu_seqlens is NULL (batch > 0) and RS_E_SHAPE when total_tokens < 0.
+ */
+rs_status rs_gdn_verify_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                               int32_t total_tokens, const void* q, const void* k,
+                               const void* v, const void* beta, const void* gate, void* state,
+                               void* ring_k, float* ring_d, float* ring_g,
+                               const int32_t* cursor, const int32_t* slot_idx, float* out,
+                               int32_t* write_pos_out, int32_t* group_counter,
+                               hipStream_t stream);
+rs_status rs_kda_verify_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                               int32_t total_tokens, const void* q, const void* k,
+                               const void* v, const void* beta, const void* gate, void* state,
+                               void* ring_k, float* ring_d, float* ring_g,
+                               const int32_t* cursor, const int32_t* slot_idx, float* out,
+                               int32_t* write_pos_out, int32_t* group_counter,
+                               hipStream_t stream);
+
+/*
  * rs_cursor_advance -- once per step, after every layer's verify (LightLLM: the shared
  * cursor is advanced only after the last layer; MTP verify trims the rejected tail).
  * For each live row r with slot s: write_pos = (cursor[s] + T > L) ? 0 : cursor[s];
@@ -147,6 +183,19 @@ rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_
                             const int32_t* slot_idx, const int32_t* accept_len,
                             rs_fold_policy policy, int32_t next_T,
                             const uint8_t* force_mask, hipStream_t stream);
+
+/*
+ * rs_cursor_advance_varlen -- rs_cursor_advance after ragged verifies: cu_seqlens and
+ * total_tokens exactly as the step's rs_*_verify_varlen calls received them.  Row r's
+ * write_pos is recomputed with its own window width T_r, and accept_len[r] is in
+ * [0, T_r] (clamped to it).  Errors as for rs_cursor_advance; also RS_E_NULLPTR when
+ * cu_seqlens is NULL (batch > 0) and RS_E_SHAPE when total_tokens < 0.
+ */
+rs_status rs_cursor_advance_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                                   int32_t total_tokens, int32_t* cursor, int32_t* fold_len,
+                                   const int32_t* slot_idx, const int32_t* accept_len,
+                                   rs_fold_policy policy, int32_t next_T,
+                                   const uint8_t* force_mask, hipStream_t stream);
 
 /*
  * rs_commit_fold -- compact commit: S[s] <- fold(S[s], ring[s, 0:fold_len[s]]) for each

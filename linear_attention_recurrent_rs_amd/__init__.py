@@ -17,6 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'commit_fold',
+           'gdn_verify_varlen', 'kda_verify_varlen', 'cursor_advance_varlen',
+           'prepare_verify_varlen', 'prepare_cursor_advance_varlen',
            'materialize', 'verify_launch_info', 'stream_read', 'library_path', 'F32', 'BF16',
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
            'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE']
@@ -62,8 +64,15 @@ def _lib():
         for name in ('rs_gdn_verify', 'rs_kda_verify'):
             getattr(lib, name).argtypes = verify_args
             getattr(lib, name).restype = ctypes.c_int
+        varlen_args = [dp, _P, ctypes.c_int32] + [_P] * 14 + [_P]
+        for name in ('rs_gdn_verify_varlen', 'rs_kda_verify_varlen'):
+            getattr(lib, name).argtypes = varlen_args
+            getattr(lib, name).restype = ctypes.c_int
         lib.rs_cursor_advance.argtypes = [dp, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int32, _P, _P]
         lib.rs_cursor_advance.restype = ctypes.c_int
+        lib.rs_cursor_advance_varlen.argtypes = [dp, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                                 ctypes.c_int, ctypes.c_int32, _P, _P]
+        lib.rs_cursor_advance_varlen.restype = ctypes.c_int
         lib.rs_commit_fold.argtypes = [dp, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P]
         lib.rs_commit_fold.restype = ctypes.c_int
         lib.rs_materialize.argtypes = [dp, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -106,9 +115,10 @@ def _check(status: int, where: str):
 
 
 def _verify_ptrs(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
-                 slot_idx, out, write_pos_out, group_counter):
+                 slot_idx, out, write_pos_out, group_counter, ntok=None):
     at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
-    BT, S, L = d.batch * d.T, d.num_slots, d.ring_cap
+    BT = d.batch * d.T if ntok is None else ntok
+    S, L = d.num_slots, d.ring_cap
     g_per = d.hv * d.dk if kda else d.hv
     args = [
         _ptr(q, 'q', BT * d.hk * d.dk, at), _ptr(k, 'k', BT * d.hk * d.dk, at),
@@ -148,6 +158,40 @@ def kda_verify(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, curs
             write_pos_out, group_counter, stream)
 
 
+def _ntok(q) -> int:
+    if q is None or q.dim() < 1:
+        raise ValueError('q must be a [total_tokens, hk, dk] tensor')
+    return int(q.shape[0])
+
+
+def _verify_varlen(kda: bool, d: Dims, cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d,
+                   ring_g, cursor, slot_idx, out, write_pos_out, group_counter, stream):
+    ntok = _ntok(q)
+    args = _verify_ptrs(kda, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                        slot_idx, out, write_pos_out, group_counter, ntok)
+    cu = _ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32)
+    name = 'rs_kda_verify_varlen' if kda else 'rs_gdn_verify_varlen'
+    _check(getattr(_lib(), name)(ctypes.byref(d), cu, ctypes.c_int32(ntok), *args,
+                                 _stream(stream)), name)
+
+
+def gdn_verify_varlen(d: Dims, cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                      cursor, slot_idx, out, write_pos_out=None, group_counter=None,
+                      stream=None):
+    """rs_gdn_verify_varlen: GDN verify with ragged windows.  Row r owns packed tokens
+    [cu_seqlens[r], cu_seqlens[r+1]) (at most d.T of them); the token count is q.shape[0]."""
+    _verify_varlen(False, d, cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                   cursor, slot_idx, out, write_pos_out, group_counter, stream)
+
+
+def kda_verify_varlen(d: Dims, cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                      cursor, slot_idx, out, write_pos_out=None, group_counter=None,
+                      stream=None):
+    """rs_kda_verify_varlen: KDA verify with ragged windows (as gdn_verify_varlen)."""
+    _verify_varlen(True, d, cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                   cursor, slot_idx, out, write_pos_out, group_counter, stream)
+
+
 def cursor_advance(d: Dims, cursor, fold_len, slot_idx, accept_len, policy: int = FOLD_NONE,
                    next_T: int = 0, force_mask=None, stream=None):
     """rs_cursor_advance: once per step, after every layer's verify."""
@@ -158,6 +202,22 @@ def cursor_advance(d: Dims, cursor, fold_len, slot_idx, accept_len, policy: int 
     fm = _ptr(force_mask, 'force_mask', d.batch, torch.uint8, optional=True)
     _check(_lib().rs_cursor_advance(ctypes.byref(d), *args, int(policy), int(next_T), fm,
                                     _stream(stream)), 'rs_cursor_advance')
+
+
+def cursor_advance_varlen(d: Dims, cu_seqlens, total_tokens: int, cursor, fold_len, slot_idx,
+                          accept_len, policy: int = FOLD_NONE, next_T: int = 0,
+                          force_mask=None, stream=None):
+    """rs_cursor_advance_varlen: the advance after ragged verifies (same cu_seqlens and
+    total token count as the step's verifies)."""
+    args = [_ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32),
+            ctypes.c_int32(int(total_tokens)),
+            _ptr(cursor, 'cursor', d.num_slots, torch.int32),
+            _ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    fm = _ptr(force_mask, 'force_mask', d.batch, torch.uint8, optional=True)
+    _check(_lib().rs_cursor_advance_varlen(ctypes.byref(d), *args, int(policy), int(next_T), fm,
+                                           _stream(stream)), 'rs_cursor_advance_varlen')
 
 
 def _fold_ptrs(d: Dims, kda: bool, state, ring_k, ring_d, ring_g):
@@ -263,4 +323,44 @@ def prepare_commit_fold(d: Dims, kda: bool, state, ring_k, ring_d, ring_g, fold_
         if st:
             raise RSError(st, 'rs_commit_fold')
     call.tensors = (state, ring_k, ring_d, ring_g, fold_len, slot_idx)
+    return call
+
+
+def prepare_verify_varlen(kda: bool, d: Dims, cu_seqlens, q, k, v, beta, gate, state, ring_k,
+                          ring_d, ring_g, cursor, slot_idx, out, write_pos_out=None,
+                          group_counter=None):
+    ntok = _ntok(q)
+    args = _verify_ptrs(kda, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                        slot_idx, out, write_pos_out, group_counter, ntok)
+    cu = _ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32)
+    name = 'rs_kda_verify_varlen' if kda else 'rs_gdn_verify_varlen'
+    fn, dref, nt = getattr(_lib(), name), ctypes.byref(d), ctypes.c_int32(ntok)
+
+    def call(stream=None):
+        st = fn(dref, cu, nt, *args, _stream(stream))
+        if st:
+            raise RSError(st, name)
+    call.dims = d
+    call.tensors = (cu_seqlens, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                    slot_idx, out, write_pos_out, group_counter)
+    return call
+
+
+def prepare_cursor_advance_varlen(d: Dims, cu_seqlens, total_tokens: int, cursor, fold_len,
+                                  slot_idx, accept_len, policy: int = FOLD_NONE,
+                                  next_T: int = 0, force_mask=None):
+    args = [_ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32),
+            ctypes.c_int32(int(total_tokens)),
+            _ptr(cursor, 'cursor', d.num_slots, torch.int32),
+            _ptr(fold_len, 'fold_len', d.num_slots, torch.int32),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    fm = _ptr(force_mask, 'force_mask', d.batch, torch.uint8, optional=True)
+    fn, dref = _lib().rs_cursor_advance_varlen, ctypes.byref(d)
+
+    def call(stream=None):
+        st = fn(dref, *args, int(policy), int(next_T), fm, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_cursor_advance_varlen')
+    call.tensors = (cu_seqlens, cursor, fold_len, slot_idx, accept_len, force_mask)
     return call

@@ -77,7 +77,10 @@ rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
   return RS_OK;
 }
 
-rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, const void* v,
+// cu_seqlens == NULL: every row verifies T tokens; else row r verifies tokens
+// [cu_seqlens[r], cu_seqlens[r + 1]) of ntok packed tokens.
+rs_status verify_impl(bool kda, const rs_dims* d, const int32_t* cu_seqlens, int32_t ntok,
+                      const void* q, const void* k, const void* v,
                       const void* beta, const void* gate, void* state, void* ring_k,
                       float* ring_d, float* ring_g, const int32_t* cursor,
                       const int32_t* slot_idx, float* out, int32_t* write_pos_out,
@@ -85,6 +88,7 @@ rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, 
   VerifyPlan plan;
   rs_status st = verify_plan(d, kda, &plan);
   if (st != RS_OK) return st;
+  if (cu_seqlens && ntok < 0) return RS_E_SHAPE;
   if (d->batch == 0) return RS_OK;
   if (!q || !k || !v || !beta || !gate || !state || !ring_k || !ring_d || !ring_g || !cursor ||
       !slot_idx || !out || !group_counter)
@@ -94,6 +98,7 @@ rs_status verify_impl(bool kda, const rs_dims* d, const void* q, const void* k, 
   a.B = d->batch; a.T = d->T; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
   a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
   a.nblocks = d->batch * d->hv * a.NV;
+  a.cu_seqlens = cu_seqlens; a.ntok = ntok;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate;
   a.state = state; a.ring_k = ring_k; a.ring_d = ring_d; a.ring_g = ring_g;
   a.cursor = cursor; a.slot_idx = slot_idx; a.out = out; a.write_pos_out = write_pos_out;
@@ -155,8 +160,8 @@ rs_status rs_gdn_verify(const rs_dims* dims, const void* q, const void* k, const
                         float* ring_d, float* ring_g, const int32_t* cursor,
                         const int32_t* slot_idx, float* out, int32_t* write_pos_out,
                         int32_t* group_counter, hipStream_t stream) {
-  return verify_impl(false, dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
-                     slot_idx, out, write_pos_out, group_counter, stream);
+  return verify_impl(false, dims, nullptr, 0, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                     cursor, slot_idx, out, write_pos_out, group_counter, stream);
 }
 
 rs_status rs_kda_verify(const rs_dims* dims, const void* q, const void* k, const void* v,
@@ -164,14 +169,38 @@ rs_status rs_kda_verify(const rs_dims* dims, const void* q, const void* k, const
                         float* ring_d, float* ring_g, const int32_t* cursor,
                         const int32_t* slot_idx, float* out, int32_t* write_pos_out,
                         int32_t* group_counter, hipStream_t stream) {
-  return verify_impl(true, dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
-                     slot_idx, out, write_pos_out, group_counter, stream);
+  return verify_impl(true, dims, nullptr, 0, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                     cursor, slot_idx, out, write_pos_out, group_counter, stream);
 }
 
-rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_len,
-                            const int32_t* slot_idx, const int32_t* accept_len,
-                            rs_fold_policy policy, int32_t next_T, const uint8_t* force_mask,
-                            hipStream_t stream) {
+rs_status rs_gdn_verify_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                               int32_t total_tokens, const void* q, const void* k,
+                               const void* v, const void* beta, const void* gate, void* state,
+                               void* ring_k, float* ring_d, float* ring_g,
+                               const int32_t* cursor, const int32_t* slot_idx, float* out,
+                               int32_t* write_pos_out, int32_t* group_counter,
+                               hipStream_t stream) {
+  if (!cu_seqlens && dims && dims->batch > 0) return RS_E_NULLPTR;
+  return verify_impl(false, dims, cu_seqlens, total_tokens, q, k, v, beta, gate, state, ring_k,
+                     ring_d, ring_g, cursor, slot_idx, out, write_pos_out, group_counter, stream);
+}
+
+rs_status rs_kda_verify_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                               int32_t total_tokens, const void* q, const void* k,
+                               const void* v, const void* beta, const void* gate, void* state,
+                               void* ring_k, float* ring_d, float* ring_g,
+                               const int32_t* cursor, const int32_t* slot_idx, float* out,
+                               int32_t* write_pos_out, int32_t* group_counter,
+                               hipStream_t stream) {
+  if (!cu_seqlens && dims && dims->batch > 0) return RS_E_NULLPTR;
+  return verify_impl(true, dims, cu_seqlens, total_tokens, q, k, v, beta, gate, state, ring_k,
+                     ring_d, ring_g, cursor, slot_idx, out, write_pos_out, group_counter, stream);
+}
+
+static rs_status advance_impl(const rs_dims* dims, const int32_t* cu_seqlens, int32_t ntok,
+                              int32_t* cursor, int32_t* fold_len, const int32_t* slot_idx,
+                              const int32_t* accept_len, rs_fold_policy policy, int32_t next_T,
+                              const uint8_t* force_mask, hipStream_t stream) {
   if (!dims) return RS_E_NULLPTR;
   if (dims->batch < 0 || dims->T < 1 || dims->T > 16 || dims->num_slots < 1 ||
       dims->ring_cap < 1 || dims->ring_cap > 256)
@@ -179,14 +208,34 @@ rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_
   if (dims->ring_cap < dims->T) return RS_E_RING_TOO_SMALL;
   if (policy < RS_FOLD_NONE || policy > RS_FOLD_FORCE) return RS_E_SHAPE;
   if (policy == RS_FOLD_LAZY && (next_T < 1 || next_T > 16)) return RS_E_SHAPE;
+  if (cu_seqlens && ntok < 0) return RS_E_SHAPE;
   if (dims->batch == 0) return RS_OK;
   if (!cursor || !fold_len || !slot_idx || !accept_len) return RS_E_NULLPTR;
   rs::AdvanceArgs a{};
   a.B = dims->batch; a.T = dims->T; a.L = dims->ring_cap; a.num_slots = dims->num_slots;
   a.policy = int(policy); a.next_T = next_T;
+  a.cu_seqlens = cu_seqlens; a.ntok = ntok;
   a.cursor = cursor; a.fold_len = fold_len; a.slot_idx = slot_idx; a.accept = accept_len;
   a.force_mask = force_mask;
   return rs::launch_advance(a, stream) == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+rs_status rs_cursor_advance(const rs_dims* dims, int32_t* cursor, int32_t* fold_len,
+                            const int32_t* slot_idx, const int32_t* accept_len,
+                            rs_fold_policy policy, int32_t next_T, const uint8_t* force_mask,
+                            hipStream_t stream) {
+  return advance_impl(dims, nullptr, 0, cursor, fold_len, slot_idx, accept_len, policy, next_T,
+                      force_mask, stream);
+}
+
+rs_status rs_cursor_advance_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
+                                   int32_t total_tokens, int32_t* cursor, int32_t* fold_len,
+                                   const int32_t* slot_idx, const int32_t* accept_len,
+                                   rs_fold_policy policy, int32_t next_T,
+                                   const uint8_t* force_mask, hipStream_t stream) {
+  if (!cu_seqlens && dims && dims->batch > 0) return RS_E_NULLPTR;
+  return advance_impl(dims, cu_seqlens, total_tokens, cursor, fold_len, slot_idx, accept_len,
+                      policy, next_T, force_mask, stream);
 }
 
 rs_status rs_commit_fold(const rs_dims* dims, int is_kda, void* state, const void* ring_k,

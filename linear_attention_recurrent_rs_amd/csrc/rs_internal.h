@@ -30,6 +30,10 @@ struct LdsLayout {
 
 struct VerifyArgs {
   int B, T, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
+  // ragged windows: row r verifies tokens [cu_seqlens[r], cu_seqlens[r + 1]) of ntok
+  // packed tokens (at most T of them); NULL = every row T tokens at r * T
+  const int32_t* cu_seqlens;
+  int ntok;
   const void* q;
   const void* k;
   const void* v;
@@ -61,12 +65,32 @@ struct FoldArgs {
 
 struct AdvanceArgs {
   int B, T, L, num_slots, policy, next_T;
+  const int32_t* cu_seqlens;   // ragged windows as in VerifyArgs, or NULL
+  int ntok;
   int32_t* cursor;
   int32_t* fold_len;
   const int32_t* slot_idx;
   const int32_t* accept;
   const uint8_t* force_mask;
 };
+
+// The verify window of a request row: its first token and its width.  Uniform windows
+// put row r's T tokens at r * T.  Ragged windows read them from the cumulative lengths,
+// clamped to the packed token count and to T, so that out-of-contract lengths stay inside
+// the caller's buffers (every kernel of a step clamps them the same way).
+__device__ __forceinline__ void row_window(const int32_t* cu, int ntok, int T, int row,
+                                           int* width, size_t* first) {
+  if (cu == nullptr) {
+    *width = T;
+    *first = (size_t)row * T;
+    return;
+  }
+  int b = cu[row], e = cu[row + 1];
+  b = b < 0 ? 0 : (b > ntok ? ntok : b);
+  e = e < b ? b : (e > ntok ? ntok : e);
+  *width = (e - b) > T ? T : (e - b);
+  *first = (size_t)b;
+}
 
 // Readout batch: window vectors (2T of them) processed per pass over the tile.
 inline int readout_vpp(int tmax) { return 2 * tmax < 8 ? 2 * tmax : 8; }

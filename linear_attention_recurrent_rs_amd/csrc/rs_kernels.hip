@@ -195,14 +195,20 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
 
-  const int T = a.T, L = a.L, dk = a.dk, dv = a.dv, hv = a.hv, hk = a.hk;
+  const int L = a.L, dk = a.dk, dv = a.dv, hv = a.hv, hk = a.hk;
   const int kh = h / a.G, col0 = vt * BV;
+  int T;
+  size_t tok0;
+  row_window(a.cu_seqlens, a.ntok, a.T, row, &T, &tok0);
   int n = a.cursor[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   const bool fold = n + T > L;                           // the window would overflow
   const int base = fold ? 0 : n;                         // write_pos
   const int nh = n;                                      // records replayed over S
-  const size_t tok0 = (size_t)row * T;
+  if (T == 0) {                                          // an empty ragged window
+    if (a.write_pos_out && h == 0 && vt == 0 && tid == 0) a.write_pos_out[row] = base;
+    return;
+  }
 
   ST* tile_raw = reinterpret_cast<ST*>(smem + a.lay.tile_raw);
   float* tile32 = reinterpret_cast<float*>(smem + a.lay.tile32);
@@ -424,9 +430,12 @@ __global__ __launch_bounds__(kThreads) void advance_kernel(AdvanceArgs a) {
   if (s < 0 || s >= a.num_slots) return;
   int n = a.cursor[s];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
+  int T;
+  size_t tok0;
+  row_window(a.cu_seqlens, a.ntok, a.T, r, &T, &tok0);
   int acc = a.accept[r];
-  acc = acc < 0 ? 0 : (acc > a.T ? a.T : acc);
-  const int base = (n + a.T > a.L) ? 0 : n;
+  acc = acc < 0 ? 0 : (acc > T ? T : acc);
+  const int base = (n + T > a.L) ? 0 : n;
   const int m = base + acc;
   int fl = 0;
   switch (a.policy) {

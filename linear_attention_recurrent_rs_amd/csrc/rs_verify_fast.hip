@@ -160,9 +160,11 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
 
-  const int T = a.T, L = a.L, hv = a.hv, hk = a.hk, dv = a.dv;
+  const int L = a.L, hv = a.hv, hk = a.hk, dv = a.dv;
   const int kh = h / a.G, col0 = vt * BV;
-  const size_t tok0 = (size_t)row * T;
+  int T;
+  size_t tok0;
+  row_window(a.cu_seqlens, a.ntok, a.T, row, &T, &tok0);
   const int XS = lay.xs_stride, CS = lay.cs;
 
   bf16* xkq = reinterpret_cast<bf16*>(smem + lay.xkq);
@@ -196,6 +198,10 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   const bool fold = n + T > L;                           // the window would overflow
   const int base = fold ? 0 : n;                         // write_pos
   const int nh = n;
+  if (T == 0) {                                          // an empty ragged window
+    if (a.write_pos_out && h == 0 && vt == 0 && tid == 0) a.write_pos_out[row] = base;
+    return;
+  }
   float beta_s[TMAX], gate_s[TMAX], Gp[TMAX];
 #pragma unroll
   for (int t = 0; t < TMAX; ++t) {

@@ -63,6 +63,23 @@ def initial(cfg: W.Config) -> Initial:
     return Initial(slots, cur, S, rk, rd, rg)
 
 
+def step_windows(cfg: W.Config, j: int):
+    """Per-row verify window widths of step j (ragged configs), else None."""
+    return W.window_lengths(cfg, j)
+
+
+def pack_windows(lens: np.ndarray, T: int):
+    """Packed-token layout of ragged windows: cumulative lengths [B + 1] and, for each
+    packed token, its index in the dense [B * T] layout (row r's first lens[r] tokens).
+    The packed buffers get one spare token row when every window is empty, so that
+    they are never empty."""
+    cu = np.zeros(len(lens) + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    idx = np.array([r * T + t for r in range(len(lens)) for t in range(int(lens[r]))], np.int64)
+    ntok = max(int(cu[-1]), 1)
+    return cu, idx, ntok
+
+
 def step_data(cfg: W.Config, j: int):
     acc = W.accept_lengths(cfg, j)
     ins = [W.step_inputs(cfg, j, layer, acc) for layer in range(cfg.layers)]
@@ -90,29 +107,65 @@ class GpuRun:
         self.out = torch.full((cfg.B * cfg.T, cfg.hv, cfg.dv), SENTINEL_OUT, dtype=torch.float32, device=dev)
         self.wp = torch.full((cfg.B,), SENTINEL_WP, dtype=torch.int32, device=dev)
 
+    def set_windows(self, lens):
+        """Ragged windows for the next verifies and advance (None: every row T tokens)."""
+        self.lens = lens
+        if lens is None:
+            return
+        cu, self.pack_idx, self.ntok = pack_windows(lens, self.cfg.T)
+        self.cu = torch.from_numpy(cu).to(self.dev)
+
+    lens = None
+
     def inputs_dev(self, inp: W.StepInputs, clean: bool = False):
         c, dev = self.cfg, self.dev
         v = inp.v_clean if clean else inp.v
         BT = c.B * c.T
-        return (to_dev(inp.q.reshape(BT, c.hk, c.dk), c.act_dtype, dev),
-                to_dev(inp.k.reshape(BT, c.hk, c.dk), c.act_dtype, dev),
-                to_dev(v.reshape(BT, c.hv, c.dv), c.act_dtype, dev),
-                to_dev(inp.beta.reshape(BT, c.hv), c.act_dtype, dev),
-                to_dev(inp.gate.reshape((BT, c.hv, c.dk) if c.kda else (BT, c.hv)), c.act_dtype, dev))
+        arrays = (inp.q.reshape(BT, c.hk, c.dk), inp.k.reshape(BT, c.hk, c.dk),
+                  v.reshape(BT, c.hv, c.dv), inp.beta.reshape(BT, c.hv),
+                  inp.gate.reshape((BT, c.hv, c.dk) if c.kda else (BT, c.hv)))
+        if self.lens is not None:
+            # packed token list: the rows' windows back to back, then spare rows of zeros
+            def pack(x):
+                p = np.zeros((self.ntok,) + x.shape[1:])
+                p[:len(self.pack_idx)] = x[self.pack_idx]
+                return p
+            arrays = tuple(pack(x) for x in arrays)
+        return tuple(to_dev(x, c.act_dtype, dev) for x in arrays)
 
     def verify(self, layer: int, dev_inputs):
         q, k, v, beta, gate = dev_inputs
-        fn = self.rs.kda_verify if self.cfg.kda else self.rs.gdn_verify
-        self.out.fill_(SENTINEL_OUT)
         self.wp.fill_(SENTINEL_WP)
-        fn(self.d, q, k, v, beta, gate, self.S[layer], self.rk[layer], self.rd[layer],
-           self.rg[layer], self.cursor, self.slots, self.out, self.wp, self.counter)
-        return self.out.clone(), self.wp.clone()
+        if self.lens is None:
+            fn = self.rs.kda_verify if self.cfg.kda else self.rs.gdn_verify
+            self.out.fill_(SENTINEL_OUT)
+            fn(self.d, q, k, v, beta, gate, self.S[layer], self.rk[layer], self.rd[layer],
+               self.rg[layer], self.cursor, self.slots, self.out, self.wp, self.counter)
+            return self.out.clone(), self.wp.clone()
+        c = self.cfg
+        fn = self.rs.kda_verify_varlen if c.kda else self.rs.gdn_verify_varlen
+        packed = torch.full((self.ntok, c.hv, c.dv), SENTINEL_OUT, dtype=torch.float32,
+                            device=self.dev)
+        fn(self.d, self.cu, q, k, v, beta, gate, self.S[layer], self.rk[layer], self.rd[layer],
+           self.rg[layer], self.cursor, self.slots, packed, self.wp, self.counter)
+        # back to the dense [B * T] layout; positions past a row's window hold the sentinel
+        out = torch.full((c.B * c.T, c.hv, c.dv), SENTINEL_OUT, dtype=torch.float32,
+                         device=self.dev)
+        if len(self.pack_idx):
+            out[torch.from_numpy(self.pack_idx).to(self.dev)] = packed[:len(self.pack_idx)]
+        if self.ntok > len(self.pack_idx):
+            assert torch.all(packed[len(self.pack_idx):] == SENTINEL_OUT), 'spare rows written'
+        return out, self.wp.clone()
 
     def advance(self, acc: np.ndarray, pol: int, next_T: int, force_mask=None):
         a = torch.from_numpy(acc.astype(np.int32)).to(self.dev)
         fm = None if force_mask is None else torch.from_numpy(force_mask.astype(np.uint8)).to(self.dev)
-        self.rs.cursor_advance(self.d, self.cursor, self.fold_len, self.slots, a, pol, next_T, fm)
+        if self.lens is None:
+            self.rs.cursor_advance(self.d, self.cursor, self.fold_len, self.slots, a, pol,
+                                   next_T, fm)
+        else:
+            self.rs.cursor_advance_varlen(self.d, self.cu, self.ntok, self.cursor, self.fold_len,
+                                          self.slots, a, pol, next_T, fm)
 
     def commit(self, layer: int):
         self.rs.commit_fold(self.d, self.cfg.kda, self.S[layer], self.rk[layer], self.rd[layer],
@@ -125,7 +178,8 @@ class GpuRun:
                             self.rg[layer], self.cursor, self.slots, out)
         return out
 
-    def step(self, acc, ins, pol, next_T, clean=False):
+    def step(self, acc, ins, pol, next_T, clean=False, lens=None):
+        self.set_windows(lens)
         outs, wps = [], []
         for layer in range(self.cfg.layers):
             o, w = self.verify(layer, self.inputs_dev(ins[layer], clean))
@@ -151,19 +205,19 @@ class OracleRun:
                                       cfg.G, cfg.L, slots=tracked) for l in range(cfg.layers)]
         self.streams = [rp.TokenStream.from_replay(ly, self.cursor) for ly in self.layers]
 
-    def step(self, acc, ins, pol, next_T, with_stream=True):
+    def step(self, acc, ins, pol, next_T, with_stream=True, lens=None):
         outs, wps = [], []
         for l, ly in enumerate(self.layers):
-            o, w = rp.verify(ly, self.cursor, self.slots, ins[l], rows=self.rows)
+            o, w = rp.verify(ly, self.cursor, self.slots, ins[l], rows=self.rows, lens=lens)
             outs.append(o); wps.append(w)
             if with_stream:
-                o2, _ = self.streams[l].verify(self.slots, ins[l], rows=self.rows)
+                o2, _ = self.streams[l].verify(self.slots, ins[l], rows=self.rows, lens=lens)
                 live = [r for r in (self.rows or range(self.cfg.B)) if self.slots[r] >= 0]
                 for r in live:
                     fin = np.isfinite(o[r])
                     assert rel_err(o[r][fin], o2[r][fin]) < 1e-9, 'oracle models disagree'
         rp.cursor_advance(self.cursor, self.fold_len, self.slots, acc, self.cfg.T, self.cfg.L,
-                          pol, next_T)
+                          pol, next_T, lens=lens)
         for ly in self.layers:
             rp.commit_fold(ly, self.fold_len, self.slots, rows=self.rows)
         if with_stream:

@@ -40,9 +40,11 @@ def _run(cfg, rows=None, steps=None, tile_v=0):
     worst = H.StepReport()
     for j in range(cfg.steps if steps is None else steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
-        print(f'[{cfg.name}] step {j} policy {pol}', flush=True)
-        g_outs, g_wps = g.step(acc, ins, pol, next_T)
-        o_outs, o_wps = o.step(acc, ins, pol, next_T)
+        lens = H.step_windows(cfg, j)
+        print(f'[{cfg.name}] step {j} policy {pol}' +
+              ('' if lens is None else f' windows {lens.tolist()}'), flush=True)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens)
+        o_outs, o_wps = o.step(acc, ins, pol, next_T, lens=lens)
         rep = H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, acc, rows, init)
         worst.out_err = max(worst.out_err, rep.out_err)
         worst.state_err = max(worst.state_err, rep.state_err)
@@ -160,3 +162,66 @@ def test_empty_batch_and_all_null():
     H.check_untouched(cfg, g, init)
     d0 = rs.Dims(0, 1, 1, 1, 16, 16, 4, 1, rs.F32, rs.F32, 0)   # empty batch: a no-op
     assert rs._lib().rs_gdn_verify(rs.ctypes.byref(d0), *([None] * 14), None) == 0
+
+
+# ----------------------------------------------------------------------------- ragged windows
+# Each row verifies its own number of draft tokens from one packed token list (cumulative
+# lengths), widths U{0..T} per row and step, so empty windows occur in every step.
+
+RAGGED = {
+    # GDN, fp32 state, staggered cursors, fused folds decided by each row's own width
+    'gdn': W.CONFIGS['ragged_gdn'].with_(B=13, null_rows=2, hk=2, hv=4),
+    # KDA, per-channel decays
+    'kda': W.CONFIGS['ragged_kda'].with_(B=7, hk=3, hv=3),
+    # spec verify flavour: bf16 state, every-commit fold, NaN/Inf in rejected drafts
+    'gdn_bf16_every_commit': W.CONFIGS['c2'].with_(B=7, hk=2, hv=4, ragged=('uniform', 0, 4)),
+    # large ring, windows up to 8 (the MFMA readout), 4 layers sharing one cursor
+    'large_ring': W.CONFIGS['c4'].with_(B=5, hk=2, hv=4, steps=20, ragged=('uniform', 0, 8)),
+    # the general kernels (dk 32, dv 48, fp32 activations)
+    'general_kernel': W.CONFIGS['ragged_gdn'].with_(B=9, null_rows=1, hk=1, hv=2, dk=32, dv=48,
+                                                    act_dtype='f32', steps=12),
+}
+
+
+@pytest.mark.parametrize('name', sorted(RAGGED))
+def test_ragged_windows(name):
+    _run(RAGGED[name])
+
+
+def test_ragged_empty_and_full_windows():
+    """Edge widths: a step where every window is empty (cursors, states and rings keep
+    their bits; write_pos = cursor), then steps where every window is full width (the
+    ragged call then gives exactly the uniform call's bits)."""
+    import linear_attention_recurrent_rs_amd as rs
+    cfg = RAGGED['gdn'].with_(steps=3)
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init)
+    o = H.OracleRun(cfg, init)
+    u = H.GpuRun(cfg, init)                      # the same workload through the uniform call
+    zeros = np.zeros(cfg.B, np.int32)
+    acc, ins, pol, next_T = H.step_data(cfg, 0)
+    S0 = [x.clone() for x in g.S]
+    cur0 = g.cursor.clone()
+    g_outs, g_wps = g.step(zeros, ins, pol, next_T, lens=zeros)
+    o_outs, o_wps = o.step(zeros, ins, pol, next_T, lens=zeros)
+    H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, zeros, list(range(cfg.B)), init)
+    live = init.slots >= 0
+    assert torch.equal(g.cursor, cur0)
+    assert all(torch.equal(a, b) for a, b in zip(g.S, S0))
+    assert torch.all(g_outs[0] == H.SENTINEL_OUT)
+    assert np.array_equal(g_wps[0].cpu().numpy()[live], init.cursor[init.slots[live]])
+    u.step(zeros, ins, pol, next_T, lens=zeros)
+    full = np.full(cfg.B, cfg.T, np.int32)
+    for j in range(1, 3):
+        acc, ins, pol, next_T = H.step_data(cfg, j)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=full)
+        u_outs, u_wps = u.step(acc, ins, pol, next_T)
+        assert torch.equal(g_outs[0], u_outs[0]) and torch.equal(g_wps[0], u_wps[0])
+        assert torch.equal(g.cursor, u.cursor) and torch.equal(g.S[0], u.S[0])
+        assert torch.equal(torch.nan_to_num(g.rd[0], nan=7.0), torch.nan_to_num(u.rd[0], nan=7.0))
+    d = g.d
+    with pytest.raises(ValueError):               # cu_seqlens of the wrong length
+        rs.gdn_verify_varlen(d, g.cu[:-1], *g.inputs_dev(ins[0]), g.S[0], g.rk[0], g.rd[0],
+                             g.rg[0], g.cursor, g.slots,
+                             torch.empty(g.ntok, cfg.hv, cfg.dv, device=g.dev), g.wp, g.counter)
+    torch.cuda.synchronize()

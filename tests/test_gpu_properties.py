@@ -164,9 +164,10 @@ def _sampled(cfg, rows, steps):
     worst = H.StepReport()
     for j in range(steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
+        lens = H.step_windows(cfg, j)
         print(f'[{cfg.name} full] step {j}', flush=True)
-        g_outs, g_wps = g.step(acc, ins, pol, next_T)
-        o_outs, o_wps = o.step(acc, ins, pol, next_T, with_stream=False)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens)
+        o_outs, o_wps = o.step(acc, ins, pol, next_T, with_stream=False, lens=lens)
         rep = H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, acc, rows, init)
         worst.out_err = max(worst.out_err, rep.out_err)
         worst.state_err = max(worst.state_err, rep.state_err)
@@ -199,3 +200,10 @@ def test_full_size_spec_verify_sampled():
 def test_full_size_kda_sampled():
     cfg = W.CONFIGS['c3'].with_(steps=8)
     _sampled(cfg, _rows(cfg, 3), cfg.steps)
+
+
+def test_full_size_ragged_sampled():
+    """Ragged windows at full size (64 rows, 16/32 heads, dk = dv = 128, ring 16, widths
+    U{0..4}, staggered cursors)."""
+    cfg = W.CONFIGS['ragged_gdn'].with_(steps=8)
+    _sampled(cfg, _rows(cfg, 4), cfg.steps)

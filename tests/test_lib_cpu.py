@@ -89,3 +89,25 @@ def test_stream_read_validation():
     assert lib.rs_stream_read(fake, 0, fake, None) == 2
     assert lib.rs_stream_read(fake, 1000, fake, None) == 2             # not a multiple of 16
     assert lib.rs_stream_read(ctypes.c_void_p(0x10008), 1024, fake, None) == 2   # misaligned
+
+
+def test_varlen_validation():
+    """The ragged-window entry points: a missing cu_seqlens is RS_E_NULLPTR, a negative
+    token count RS_E_SHAPE, and dimension errors are reported as for the uniform calls."""
+    lib = rs._lib()
+    fake = ctypes.c_void_p(256)            # never dereferenced: validation fails first
+    d = _dims(T=4)
+    dk = _dims(T=4, hk=4)
+    assert lib.rs_gdn_verify_varlen(ctypes.byref(d), None, 8, *([None] * 14), None) == 1
+    assert lib.rs_kda_verify_varlen(ctypes.byref(dk), None, 8, *([None] * 14), None) == 1
+    assert lib.rs_gdn_verify_varlen(ctypes.byref(d), fake, -1, *([None] * 14), None) == 2
+    assert lib.rs_kda_verify_varlen(ctypes.byref(dk), fake, -1, *([None] * 14), None) == 2
+    bad = _dims(T=0)
+    assert lib.rs_gdn_verify_varlen(ctypes.byref(bad), fake, 8, *([None] * 14), None) == 2
+    adv = lib.rs_cursor_advance_varlen
+    assert adv(ctypes.byref(d), None, 8, *([None] * 4), 0, 0, None, None) == 1
+    assert adv(ctypes.byref(d), fake, -1, *([None] * 4), 0, 0, None, None) == 2
+    assert adv(ctypes.byref(_dims(T=4, ring_cap=3)), fake, 8, *([None] * 4), 0, 0, None,
+               None) == 4
+    empty = _dims(batch=0)
+    assert lib.rs_gdn_verify_varlen(ctypes.byref(empty), None, 0, *([None] * 14), None) == 0

@@ -49,6 +49,8 @@ class Config:
     cursor_init: str = 'zero'    # 'zero' | 'stagger' (cursor = row mod L, ring prefilled)
     policy: str = 'none'         # 'none' | 'every_commit' | 'c4_schedule'
     extra_slots: int = 16
+    ragged: tuple = ()           # () = every row verifies T tokens; ('uniform', lo, hi) =
+                                 # per-row window widths U{lo..hi} (packed token list)
 
     @property
     def G(self) -> int:
@@ -86,6 +88,18 @@ CONFIGS = {
                  state_dtype='f32', act_dtype='bf16', L=64, T=8, accept=('binomial', 8, 0.7),
                  steps=32, layers=4, seed=4, policy='c4_schedule'),
 }
+
+
+# Ragged verify windows (packed per-request verify lengths), beside the five workloads:
+# GDN and KDA layers of the same shapes, widths U{0..4} per row and step, staggered cursors.
+CONFIGS['ragged_gdn'] = Config('ragged_gdn', False, B=64, null_rows=4, hk=16, hv=32, dk=128,
+                               dv=128, state_dtype='f32', act_dtype='bf16', L=16, T=4,
+                               accept=('uniform', 0, 4), steps=16, seed=5,
+                               cursor_init='stagger', ragged=('uniform', 0, 4))
+CONFIGS['ragged_kda'] = Config('ragged_kda', True, B=64, null_rows=0, hk=32, hv=32, dk=128,
+                               dv=128, state_dtype='f32', act_dtype='bf16', L=16, T=4,
+                               accept=('uniform', 0, 4), steps=16, seed=6,
+                               cursor_init='stagger', ragged=('uniform', 0, 4))
 
 
 def step_policy(cfg: Config, step: int):
@@ -133,7 +147,7 @@ def _rng(cfg: Config, *purpose: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([cfg.seed, *purpose]))
 
 
-_P_SLOTS, _P_STATE, _P_RING, _P_TOKENS, _P_ACCEPT, _P_NAN = 1, 2, 3, 4, 5, 6
+_P_SLOTS, _P_STATE, _P_RING, _P_TOKENS, _P_ACCEPT, _P_NAN, _P_WINDOW = 1, 2, 3, 4, 5, 6, 7
 
 
 def _unit(rng, shape):
@@ -203,8 +217,19 @@ def initial_ring(cfg: Config, cursor: np.ndarray, layer: int = 0, fill=np.nan):
     return rk, rd, rg
 
 
+def window_lengths(cfg: Config, step: int) -> Optional[np.ndarray]:
+    """int32 [B]: each row's verify window width at ``step`` (ragged configs), else None."""
+    if not cfg.ragged:
+        return None
+    kind, lo, hi = cfg.ragged
+    if kind != 'uniform':
+        raise ValueError(kind)
+    rng = _rng(cfg, _P_WINDOW, step)
+    return np.clip(rng.integers(lo, hi + 1, size=cfg.B), 0, cfg.T).astype(np.int32)
+
+
 def accept_lengths(cfg: Config, step: int) -> np.ndarray:
-    """int32 [B] in [0, T], drawn before the step's verify."""
+    """int32 [B] in [0, T] (ragged: in [0, T_r]), drawn before the step's verify."""
     rng = _rng(cfg, _P_ACCEPT, step)
     kind = cfg.accept[0]
     if kind == 'const':
@@ -215,7 +240,11 @@ def accept_lengths(cfg: Config, step: int) -> np.ndarray:
         a = rng.binomial(cfg.accept[1], cfg.accept[2], size=cfg.B)
     else:
         raise ValueError(kind)
-    return np.clip(a, 0, cfg.T).astype(np.int32)
+    a = np.clip(a, 0, cfg.T)
+    lens = window_lengths(cfg, step)
+    if lens is not None:
+        a = np.minimum(a, lens)
+    return a.astype(np.int32)
 
 
 @dataclass
