@@ -23,8 +23,9 @@ sample of the same workload, single-threaded.
 extra: the T = 3 case; the T = 1 verify at three history states (none, steady, every row
 folding); and full step loops (verify per layer, cursor advance, commit folds by policy)
 of the spec-verify (batch 128, bf16 state, T = 4, fold every commit), KDA (batch 64, T = 3)
-and large-ring (batch 256, ring 64, T = 8, 4 layers, forced commit folds) workloads, each
-with verify and commit-fold kernel times and verified / committed tokens per second.
+and large-ring (batch 256, ring 64, T = 8, 4 layers, forced commit folds) workloads and of
+ragged GDN and KDA verifies (batch 64, widths U{0..4} per row from one packed token list),
+each with verify and commit-fold kernel times and verified / committed tokens per second.
 """
 from __future__ import annotations
 
@@ -255,7 +256,7 @@ def cpu_baseline(T: int, budget_s: float = 12.0):
 # the same shapes and distributions (unit q/k rows, v ~ N(0,1), beta ~ U(0,1), gates
 # exp(-softplus(N(0,1)))), so that the benchmark does not spend minutes building fp64 data.
 
-def _rand_setup(cfg, layers, seed=1234):
+def _rand_setup(cfg, layers, seed=1234, tile_v=0):
     import torch
     import linear_attention_recurrent_rs_amd as rs
     import workloads as W
@@ -288,7 +289,7 @@ def _rand_setup(cfg, layers, seed=1234):
                 gates(BT, *gsh).to(bf))
     slots_np = W.slot_map(cfg)
     d = rs.Dims(cfg.B, cfg.T, cfg.hk, cfg.hv, cfg.dk, cfg.dv, L, ns, rs.BF16,
-                rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, 0)
+                rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, tile_v)
     st.update(slots_np=slots_np, slots=torch.from_numpy(slots_np.astype(np.int32)).to(dev),
               inputs=inputs, d=d, dev=dev)
     return st
@@ -359,7 +360,7 @@ def stream_reference(nbytes, pools=8, iters=48):
     return {'bytes': n * 4, 'us': round(us, 3), 'gbs': round(n * 4 / us / 1e3, 1)}
 
 
-def run_workload(name, steps=30, warmup=10):
+def run_workload(name, steps=30, warmup=10, tile_v=0):
     """A full step loop of another workload: a verify per layer, the cursor advance, and the
     commit folds its policy asks for.  Verify and commit-fold kernel times from HIP events;
     verified tokens/s per layer = live * T * layers / step time; committed tokens/s per
@@ -369,7 +370,7 @@ def run_workload(name, steps=30, warmup=10):
     import workloads as W
     cfg = W.CONFIGS[name]
     layers = cfg.layers
-    st = _rand_setup(cfg, layers)
+    st = _rand_setup(cfg, layers, tile_v=tile_v)
     dev, slots_np, d = st['dev'], st['slots_np'], st['d']
     cursor = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
     fold_len = torch.zeros_like(cursor)
@@ -377,19 +378,38 @@ def run_workload(name, steps=30, warmup=10):
     out = torch.empty(cfg.B * cfg.T, cfg.hv, cfg.dv, device=dev)
     n_sets = 4
     sets = [st['inputs']() for _ in range(n_sets)]
-    verify = [[rs.prepare_verify(cfg.kda, d, *sets[j], st['S'][l], st['rk'][l], st['rd'][l],
-                                 st['rg'][l], cursor, st['slots'], out, None, counter)
-               for l in range(layers)] for j in range(n_sets)]
-    commit = [rs.prepare_commit_fold(d, cfg.kda, st['S'][l], st['rk'][l], st['rd'][l],
-                                     st['rg'][l], fold_len, st['slots']) for l in range(layers)]
     total = warmup + steps
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
     accs = [W.accept_lengths(cfg, j) for j in range(total)]
     acc_d = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in accs]
     pols = [W.step_policy(cfg, j) for j in range(total)]
-    adv = [rs.prepare_cursor_advance(d, cursor, fold_len, st['slots'], acc_d[j], pols[j][0],
-                                     pols[j][1]) for j in range(total)]
+    if cfg.ragged:
+        # ragged windows: each step packs its rows' windows (widths drawn per row and step)
+        # into the leading rows of the input buffers, with cumulative lengths on the device
+        lens = [W.window_lengths(cfg, j) for j in range(total)]
+        cus = [np.concatenate([[0], np.cumsum(x)]).astype(np.int32) for x in lens]
+        cu_d = [torch.from_numpy(c).to(dev) for c in cus]
+        ntok = [max(int(c[-1]), 1) for c in cus]
+        verify = [[rs.prepare_verify_varlen(cfg.kda, d, cu_d[j],
+                                            *[x[:ntok[j]] for x in sets[j % n_sets]],
+                                            st['S'][l], st['rk'][l], st['rd'][l], st['rg'][l],
+                                            cursor, st['slots'], out[:ntok[j]], None, counter)
+                   for l in range(layers)] for j in range(total)]
+        adv = [rs.prepare_cursor_advance_varlen(d, cu_d[j], ntok[j], cursor, fold_len,
+                                                st['slots'], acc_d[j], pols[j][0], pols[j][1])
+               for j in range(total)]
+        verified = [sum(int(lens[j][r]) for r in live) for j in range(total)]
+    else:
+        verify = [[rs.prepare_verify(cfg.kda, d, *sets[j % n_sets], st['S'][l], st['rk'][l],
+                                     st['rd'][l], st['rg'][l], cursor, st['slots'], out, None,
+                                     counter)
+                   for l in range(layers)] for j in range(n_sets)]
+        adv = [rs.prepare_cursor_advance(d, cursor, fold_len, st['slots'], acc_d[j], pols[j][0],
+                                         pols[j][1]) for j in range(total)]
+        verified = [len(live) * cfg.T] * total
+    commit = [rs.prepare_commit_fold(d, cfg.kda, st['S'][l], st['rk'][l], st['rd'][l],
+                                     st['rg'][l], fold_len, st['slots']) for l in range(layers)]
     stream = torch.cuda.current_stream()
-    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
     ev_v, ev_c = [], []
 
     def step(j, timed):
@@ -397,7 +417,7 @@ def run_workload(name, steps=30, warmup=10):
             if timed:
                 e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 e[0].record(stream)
-            verify[j % n_sets][l](stream)
+            verify[j % len(verify)][l](stream)
             if timed:
                 e[1].record(stream)
                 ev_v.append(e)
@@ -423,8 +443,10 @@ def run_workload(name, steps=30, warmup=10):
     step_s = (t1 - t0) / steps
     acc_per_step = float(np.mean([sum(int(accs[j][r]) for r in live) for j in range(warmup, total)]))
     res = {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'ring': cfg.L, 'layers': layers,
+           'windows': f'ragged U{{{cfg.ragged[1]}..{cfg.ragged[2]}}}' if cfg.ragged else 'T',
            'kda': cfg.kda, 'state': cfg.state_dtype, 'ms_per_step': round(step_s * 1e3, 5),
-           'verified_tokens_per_s_per_layer': round(len(live) * cfg.T * layers / step_s / layers, 1),
+           'verified_tokens_per_s_per_layer':
+               round(float(np.mean(verified[warmup:])) / step_s, 1),
            'committed_tokens_per_s_per_layer': round(acc_per_step / step_s, 1),
            'verify_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_v])) * 1e3, 3)}
     if ev_c:
@@ -449,7 +471,8 @@ def main():
     ap.add_argument('--no-extra', action='store_true',
                     help='skip the history states and the other workloads')
     ap.add_argument('--only-workload', default='',
-                    help='run one of the other workloads (c2, c3, c4) alone and exit')
+                    help='run one of the other workloads (c2, c3, c4, ragged_gdn, '
+                         'ragged_kda) alone and exit')
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -462,7 +485,7 @@ def main():
         sys.exit(2)
 
     if args.only_workload:
-        print(json.dumps(run_workload(args.only_workload)), flush=True)
+        print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -519,7 +542,7 @@ def main():
             extra[f'history_states_T{T}'] = history_states(T)
             print(f'# history states T={T}: {extra[f"history_states_T{T}"]}', file=sys.stderr,
                   flush=True)
-        for name in ('c2', 'c3', 'c4'):
+        for name in ('c2', 'c3', 'c4', 'ragged_gdn', 'ragged_kda'):
             extra[name] = run_workload(name)
             print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
     if extra:

@@ -117,11 +117,12 @@ __device__ __forceinline__ void store_tile(ST* so, const f4 (&s)[QPT][4], int rg
 // Workgroups per CU the register cap is set for.  More resident workgroups keep more tile
 // bytes in flight, so the cap is raised where that fits without spills and measures
 // faster: six per CU (at most 80 VGPRs) for 64-column tiles at windows 2-3 (KDA: 2), five
-// (96 VGPRs) for the other 64-column tiles up to window 3, four (128 VGPRs) for
-// 128-column bf16 tiles up to window 3.  (At window 1 six per CU fit too but run slower.)
+// (96 VGPRs) for the other 64-column tiles up to window 3 and GDN's at window 4, four (128
+// VGPRs) for 128-column bf16 tiles up to window 3.  (At window 1 six per CU fit too but
+// run slower; KDA at window 4 would spill under five.)
 constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
   return (bv <= 64 && (tmax == 2 || (tmax == 3 && !kda))) ? 6
-         : (bv <= 64 && tmax <= 3)                         ? 5
+         : (bv <= 64 && (tmax <= 3 || (tmax == 4 && !kda))) ? 5
          : (bv == 128 && bf16_state && tmax <= 3)          ? 4
                                                            : 1;
 }
