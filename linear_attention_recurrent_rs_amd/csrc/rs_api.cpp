@@ -67,7 +67,8 @@ rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
     p->fast = use_fast(d, p->bv);
     // the fast verify is compiled for every window up to 4 and for 8 and 16 beyond
     p->tmax = (p->fast && d->T <= 4) ? d->T : tmax_of(d->T);
-    if (p->fast) p->flay = rs::fast_layout(kda, p->bv, p->tmax, d->T, d->ring_cap);
+    if (p->fast) p->flay = rs::fast_layout(kda, d->state_dtype == RS_BF16, p->bv, p->tmax, d->T,
+                                           d->ring_cap);
     else p->lay = rs::verify_layout(kda, dbytes(d->state_dtype), p->bv, p->tmax, d->T, d->dk,
                                     d->ring_cap);
     if (p->lds() <= kMaxLds || d->tile_v != 0 || p->bv <= 16) break;

@@ -165,7 +165,13 @@ struct FastLayout {
 
 constexpr int kKeyStride = 136;   // 128 bf16 + 16 bytes of padding
 
-inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
+// The fast verify's readout on bf16 MFMAs: GDN, a bf16 state, 128-column tiles, windows
+// 2..8 (at most 16 readout vectors).
+__host__ __device__ constexpr bool fast_bf16_mfma(bool kda, bool bf16_state, int bv, int tmax) {
+  return !kda && bf16_state && bv == 128 && tmax >= 2 && tmax <= 8;
+}
+
+inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T, int L) {
   auto al = [](int x) { return (x + 15) & ~15; };
   const int dk = 128, vpp = readout_vpp(tmax), ks = kKeyStride;
   FastLayout l{};
@@ -186,9 +192,18 @@ inline FastLayout fast_layout(bool kda, int bv, int tmax, int T, int L) {
   l.xs = o; o += kda ? al(2 * tmax * l.xs_stride * 4) : 0;
   l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
   l.C = o; o += al((kda ? 4 : 1) * l.lp * l.cs * 4);
-  // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readout)
-  l.red = o; o += al(4 * ((bv == 64 && tmax >= 8) ? l.nvec_pad : vpp) * bv * 4);
-  l.hist = o; o += (bv == 64 && tmax >= 8) ? al(l.nvec_pad * bv * 4) : 0;
+  // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readouts).  The
+  // bf16 MFMA readout writes them after its last read of the history records, keys, scores
+  // and readout vectors, so it reuses that region when it is large enough.
+  const bool bfm = fast_bf16_mfma(kda, bf16_state, bv, tmax);
+  const bool all_vec = (bv == 64 && tmax >= 8) || bfm;
+  const int red_bytes = al(4 * (all_vec ? l.nvec_pad : vpp) * bv * 4);
+  if (bfm && o - l.hkeys >= red_bytes) {
+    l.red = l.hkeys;
+  } else {
+    l.red = o; o += red_bytes;
+  }
+  l.hist = o; o += all_vec ? al(l.nvec_pad * bv * 4) : 0;
   l.Am = o; o += al(tmax * tmax * 4);
   l.Qm = o; o += al(tmax * tmax * 4);
   l.total = o;

@@ -123,8 +123,20 @@ __device__ __forceinline__ void store_tile(ST* so, const f4 (&s)[QPT][4], int rg
 constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
   return (bv <= 64 && (tmax == 2 || (tmax == 3 && !kda))) ? 6
          : (bv <= 64 && (tmax <= 3 || (tmax == 4 && !kda))) ? 5
+         : fast_bf16_mfma(kda, bf16_state, bv, tmax)       ? 5
          : (bv == 128 && bf16_state && tmax <= 3)          ? 4
                                                            : 1;
+}
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Element p (0..7) of four rows' 8-column chunks (one per row, 4 dwords of bf16 pairs),
+// packed as four bf16 K entries (rows 0..3) of an MFMA operand.
+__device__ __forceinline__ s4 column_of(const u4 (&r)[4], int p) {
+  const int q = p >> 1, sh = (p & 1) * 16;
+  const uint32_t e0 = (r[0][q] >> sh) & 0xffffu, e1 = (r[1][q] >> sh) & 0xffffu;
+  const uint32_t e2 = (r[2][q] >> sh) & 0xffffu, e3 = (r[3][q] >> sh) & 0xffffu;
+  return __builtin_bit_cast(s4, u2{e0 | (e1 << 16), e2 | (e3 << 16)});
 }
 
 template <bool KDA, typename ST, int BV, int TMAX>
@@ -142,6 +154,12 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   static_assert(QPT >= 1 && DK % (4 * RG) == 0 && CC >= 8 && CC <= 32, "tile split");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
+  // GDN with a bf16 state and 128-column tiles: every readout vector is a scalar times a
+  // bf16 input (q_t or k_t), so the readout runs on bf16 MFMAs with exact products, the
+  // state straight from its loaded bytes (step 8).  A 16-lane group loads whole 256-byte
+  // rows (8 columns a lane); wave w holds rows 32w + 16j + 4g + i (g = lane / 16, i < 4).
+  constexpr bool BF16_MFMA = fast_bf16_mfma(KDA, sizeof(ST) == 2, BV, TMAX);
+  constexpr int NTILE = BF16_MFMA ? 8 : QPT * 4;          // tile load instructions
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Lane mapping.  Column quad fastest (cc = lane % CC) makes 16 consecutive lanes read
   // one whole 256-byte row segment, the best load order; the MFMA readout needs it too
@@ -230,14 +248,25 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   // 3. the state tile: HBM -> registers, the last vector loads issued before the wait
   const ST* sg = static_cast<const ST*>(a.state) + (((size_t)slot * hv + h) * DK) * dv + col0;
   f4 s[QPT][4];
+  u4 raw[2][4];
+  if constexpr (BF16_MFMA) {
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[j][i] = load4_nt(sg + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc));
+      for (int i = 0; i < 4; ++i)
+        raw[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
+            sg + (uint32_t)((32 * wave + 16 * j + 4 * (lane >> 4) + i) * dv + 8 * (lane & 15))));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s[j][i] = load4_nt(sg + (uint32_t)((4 * (rg + RG * j) + i) * dv + 4 * cc));
+    }
   }
   code_fence();
-  lds_barrier<QPT * 4>();                                // every copy but the tile is in LDS
+  lds_barrier<NTILE>();                                  // every copy but the tile is in LDS
   // fp32 state, on a fold: the arrival of this workgroup at its key group's counter (step 7
   // explains it), now that its reads of the ring are complete, so that the round trip of
   // the atomic overlaps the scores.  (bf16 state arrives in step 7: the result, read
@@ -448,7 +477,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
   //   the history part, step 8.)
   const int NP = lay.nvec_pad;
-  if (MFMA_READOUT && hrows > 0) {
+  if ((MFMA_READOUT || BF16_MFMA) && hrows > 0) {
     constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -504,7 +533,46 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = __shfl(arrived, 0) == a.G * a.NV - 1;
   }
-  if (fold) {
+  if (fold && BF16_MFMA) {
+    // S <- Gam (.) S + sum_i gamma_i k_i d_i^T in fp32, four rows at a time, then one
+    // bf16 rounding: the rounded bytes are written back and kept for the readout
+    ST* so = static_cast<ST*>(a.state) + (((size_t)slot * hv + h) * DK) * dv + col0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r0 = 32 * wave + 16 * j + 4 * (lane >> 4);
+      float f[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[i][2 * q] = __uint_as_float(raw[j][i][q] << 16) * Gam;
+          f[i][2 * q + 1] = __uint_as_float(raw[j][i][q] & 0xffff0000u) * Gam;
+        }
+      }
+      for (int rec = 0; rec < nh; ++rec) {
+        const f4 d0 = load4(hd + rec * BV + 8 * (lane & 15));
+        const f4 d1 = load4(hd + rec * BV + 8 * (lane & 15) + 4);
+        const f4 kq = bf16x4(hkeys + rec * KS + r0) * gam_i[rec];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            f[i][c] += kq[i] * d0[c];
+            f[i][4 + c] += kq[i] * d1[c];
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          raw[j][i][q] = uint32_t(bf16_rne(f[i][2 * q])) |
+                         (uint32_t(bf16_rne(f[i][2 * q + 1])) << 16);
+        __builtin_nontemporal_store(
+            raw[j][i], reinterpret_cast<u4*>(so + (uint32_t)((r0 + i) * dv + 8 * (lane & 15))));
+      }
+    }
+  } else if (fold) {
     // S <- Gam (.) S + sum_i gamma_i k_i d_i^T in the registers, then one write
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
@@ -545,7 +613,54 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   float Pv[NV2];
 #pragma unroll
   for (int m = 0; m < NV2; ++m) Pv[m] = 0.f;
-  if constexpr (MFMA_READOUT) {
+  if constexpr (BF16_MFMA) {
+    // R_v = S^T x_v for the raw inputs x_v = xkq row v (q_0.., then k_0..) on bf16 MFMAs:
+    // A = 16 vectors x this lane group's 4 rows, B = the same 4 rows x 16 columns
+    // (column 8 n + p of the tile in MFMA p).  Lane l ends with vector 4 (l / 16) + e at
+    // columns 8 (l % 16) + p in element e of accumulator p; P = (scale G_t) R + history.
+    const int lc = lane & 15, lg = lane >> 4;
+    f4 D[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) D[p] = f4{0.f, 0.f, 0.f, 0.f};
+    const s4 zero4 = s4{0, 0, 0, 0};
+    const bool vok = lc < nvec;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const s4 xa = *reinterpret_cast<const s4*>(xkq + (vok ? lc : 0) * KS + 32 * wave + 16 * j +
+                                                 4 * lg);
+      const s4 av = vok ? xa : zero4;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) D[p] = mfma_bf16_16x16x16(av, column_of(raw[j], p), D[p]);
+    }
+    // per-wave partial sums to LDS, in readout order (q_t at 2t, k_t at 2t + 1).  The
+    // buffer reuses the history records, which every wave has finished reading here.
+    const int NPd = lay.nvec_pad;
+    lds_barrier();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * lg + e;
+      if (v < nvec) {
+        const int m = v < T ? 2 * v : 2 * (v - T) + 1;
+        float* dst = red + (wave * NPd + m) * BV + 8 * lc;
+        store4(dst, f4{D[0][e], D[1][e], D[2][e], D[3][e]});
+        store4(dst + 4, f4{D[4][e], D[5][e], D[6][e], D[7][e]});
+      }
+    }
+    lds_barrier();
+    if (tid < BV) {
+      const float scale = fold ? 1.f : Gam;
+#pragma unroll
+      for (int m = 0; m < NV2; ++m) {
+        if (m < nvec) {
+          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
+                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
+          p *= scale * Gp[m >> 1];
+          if (hrows > 0) p += hist[m * BV + tid];
+          Pv[m] = p;
+        }
+      }
+    }
+  } else if constexpr (MFMA_READOUT) {
     // Many window vectors: an MFMA contraction over the tile rows.  The registers are
     // already an A operand: lane l holds column 4*(l%16) + jj of the rows of row group
     // 4*wave + l/16, so for fixed (j, i, jj) A[m][k] = S[row(k)][4m + jj] with K = the

@@ -115,6 +115,16 @@ def test_wide_windows(T, L):
     _run(cfg)
 
 
+@pytest.mark.parametrize('T', [2, 3, 4, 8])
+def test_bf16_state_history_and_fused_folds(T):
+    """bf16 state, 128-column tiles (the readout on bf16 MFMAs), no commit folds: rows
+    replay up to L - T history records and fold in-verify when the ring would overflow,
+    with staggered cursors."""
+    cfg = W.CONFIGS['c2'].with_(B=6, hk=2, hv=4, T=T, accept=('uniform', 1, T), policy='none',
+                                nan_frac=0.0, cursor_init='stagger', steps=14)
+    _run(cfg)
+
+
 def test_odd_shapes():
     """dk=dv=16 (one 16-wide tile), dv=48 (three 16-wide tiles), dk=64, ring == window."""
     _run(W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=16, dv=48, L=3, T=3, accept=('uniform', 0, 3),
