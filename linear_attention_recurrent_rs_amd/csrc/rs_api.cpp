@@ -120,9 +120,29 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   const bool kda = is_kda != 0;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
   int bv = choose_bv(d);
+  // dk = 128 with bf16 keys and a bf16 state, in whole 128-column rows: the row-coalesced
+  // fold (rs_fold_fast.hip fold_bf16_kernel), when its records fit in LDS
+  if (d->state_dtype == RS_BF16 && (d->tile_v == 0 || d->tile_v == 128) && d->dv % 128 == 0 &&
+      use_fast(d, 128)) {
+    const rs::FoldFastLayout flay = rs::fold_fast_layout(kda, 128, d->ring_cap);
+    if (flay.total <= kMaxLds) {
+      if (d->batch == 0) return RS_OK;
+      if (!state_in || !state_out || !ring_k || !ring_d || !ring_g || !nrec || !slot_idx)
+        return RS_E_NULLPTR;
+      rs::FoldArgs a{};
+      a.B = d->batch; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
+      a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / 128; a.num_slots = d->num_slots;
+      a.nblocks = d->batch * d->hv * a.NV;
+      a.state_in = state_in; a.state_out = state_out; a.ring_k = ring_k; a.ring_d = ring_d;
+      a.ring_g = ring_g; a.nrec = nrec; a.slot_idx = slot_idx;
+      return rs::launch_fold_bf16(kda, materialize, a, flay, stream) == hipSuccess ? RS_OK
+                                                                                 : RS_E_LAUNCH;
+    }
+  }
   // dk = 128 with bf16 keys and an fp32 state: the register-tile MFMA fold
   // (rs_fold_fast.hip).  A bf16 state would reach those registers by 8-byte loads, 32-byte
-  // row pieces per 16-column block, so it takes the LDS-staged fold (rs_kernels.hip).
+  // row pieces per 16-column block; it takes the fold above or the LDS-staged fold
+  // (rs_kernels.hip).
   const bool f32_state = d->state_dtype == RS_F32;
   bool fast = false;
   rs::FoldFastLayout flay{};

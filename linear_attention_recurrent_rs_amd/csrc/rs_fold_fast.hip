@@ -135,6 +135,145 @@ __global__ __launch_bounds__(kThreads) void fold_fast_kernel(FoldArgs a, FoldFas
   }
 }
 
+// Commit fold and materialize of a bf16 state in 128-column tiles.  The MFMA fold above
+// keeps the tile as MFMA accumulators, whose lane layout would read a bf16 row in 32-byte
+// pieces.  Here a 16-lane group reads whole 256-byte rows (8 columns a lane; wave w holds
+// rows 32w + 16j + 4g + i, g = lane / 16), and the rank-nrec update runs on the VALU in
+// fp32, four rows at a time, with one bf16 rounding per element at the end.  Same method,
+// records and decays as fold_fast_kernel.
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+template <bool KDA, bool MATERIALIZE>
+__global__ __launch_bounds__(kThreads, 4) void fold_bf16_kernel(FoldArgs a, FoldFastLayout lay) {
+  constexpr int DK = 128, KS = kKeyStride, BV = 128;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lc = lane & 15, lg = lane >> 4;
+  const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
+  const int vt = lid % a.NV;
+  const int h = (lid / a.NV) % a.hv;
+  const int row = lid / (a.NV * a.hv);
+  const int slot = a.slot_idx[row];
+  if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
+  const int L = a.L, dv = a.dv, hv = a.hv, hk = a.hk;
+  int n = a.nrec[slot];
+  n = n < 0 ? 0 : (n > L ? L : n);
+  if (!MATERIALIZE && n == 0) return;                   // nothing to commit
+  const int kh = h / a.G, col0 = vt * BV;
+
+  bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
+  float* hd = reinterpret_cast<float*>(smem + lay.hd);
+  float* hg = reinterpret_cast<float*>(smem + lay.hg);
+  float* gam_i = reinterpret_cast<float*>(smem + lay.gam_i);
+  float* Gamv = reinterpret_cast<float*>(smem + lay.Gam);
+
+  // 1. records [0, n) -> LDS, asynchronous
+  if (n > 0) {
+    const bf16* rkg = static_cast<const bf16*>(a.ring_k);
+    dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, n, hkeys,
+                 KS * 2);
+    dma_rows(a.ring_d + ((size_t)slot * L * hv + h) * dv + col0, (size_t)hv * dv * 4, BV * 4, n,
+             hd);
+    if (KDA)
+      dma_rows(a.ring_g + ((size_t)slot * L * hv + h) * DK, (size_t)hv * DK * 4, DK * 4, n, hg);
+    else
+      dma_words(a.ring_g + (size_t)slot * L * hv + h, (size_t)hv * 4, n, hg);
+  }
+  code_fence();
+
+  // 2. the state tile -> registers, 16 bytes (8 bf16) per load
+  const bf16* src =
+      static_cast<const bf16*>(a.state_in) + (((size_t)slot * hv + h) * DK) * dv + col0;
+  u4 raw[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      raw[j][i] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(
+          src + (uint32_t)((32 * wave + 16 * j + 4 * lg + i) * dv + 8 * lc)));
+  }
+  code_fence();
+  lds_barrier<8>();                                      // the records are in LDS
+
+  // 3. decays, as in fold_fast_kernel
+  float Gam = 1.f;
+  if (!KDA) {
+    for (int i = 0; i < n; ++i) Gam *= hg[i];
+    for (int i = tid; i < n; i += kThreads) {
+      float g = 1.f;
+      for (int j = i + 1; j < n; ++j) g *= hg[j];
+      gam_i[i] = g;
+    }
+  } else if (tid < DK) {
+    float g = 1.f;
+    for (int i = n - 1; i >= 0; --i) {
+      const float al = hg[i * DK + tid];
+      hg[i * DK + tid] = g * to_f32(hkeys[i * KS + tid]);
+      g *= al;
+    }
+    Gamv[tid] = g;
+  }
+  lds_barrier();
+
+  // 4. S <- Gam (.) S + sum_i khat_i d_i^T, four rows at a time, then one write
+  bf16* dst16 = static_cast<bf16*>(a.state_out) + (((size_t)slot * hv + h) * DK) * dv + col0;
+  float* dst32 = static_cast<float*>(a.state_out) + (((size_t)row * hv + h) * DK) * dv + col0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r0 = 32 * wave + 16 * j + 4 * lg;
+    float f[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gr = KDA ? Gamv[r0 + i] : Gam;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[i][2 * q] = __uint_as_float(raw[j][i][q] << 16) * gr;
+        f[i][2 * q + 1] = __uint_as_float(raw[j][i][q] & 0xffff0000u) * gr;
+      }
+    }
+    for (int rec = 0; rec < n; ++rec) {
+      const f4 d0 = load4(hd + rec * BV + 8 * lc);
+      const f4 d1 = load4(hd + rec * BV + 8 * lc + 4);
+      const f4 kq = KDA ? load4(hg + rec * DK + r0)
+                        : load4(hkeys + rec * KS + r0) * gam_i[rec];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          f[i][c] += kq[i] * d0[c];
+          f[i][4 + c] += kq[i] * d1[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)((r0 + i) * dv + 8 * lc);
+      if constexpr (MATERIALIZE) {
+        store4_nt(dst32 + off, f4{f[i][0], f[i][1], f[i][2], f[i][3]});
+        store4_nt(dst32 + off + 4, f4{f[i][4], f[i][5], f[i][6], f[i][7]});
+      } else {
+        u4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = uint32_t(bf16_rne(f[i][2 * q])) | (uint32_t(bf16_rne(f[i][2 * q + 1])) << 16);
+        __builtin_nontemporal_store(w, reinterpret_cast<u4*>(dst16 + off));
+      }
+    }
+  }
+}
+
+hipError_t launch_fold_bf16(bool kda, bool materialize, const FoldArgs& a,
+                            const FoldFastLayout& lay, hipStream_t s) {
+  auto k = kda ? (materialize ? fold_bf16_kernel<true, true> : fold_bf16_kernel<true, false>)
+               : (materialize ? fold_bf16_kernel<false, true> : fold_bf16_kernel<false, false>);
+  if (lay.total > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
+  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), lay.total, s, a, lay);
+  return hipGetLastError();
+}
+
 template <bool KDA, typename ST, int BV, bool MAT>
 static hipError_t run_fold_fast(const FoldArgs& a, const FoldFastLayout& lay, hipStream_t s) {
   using OT = typename std::conditional<MAT, float, ST>::type;

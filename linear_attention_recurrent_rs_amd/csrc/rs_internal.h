@@ -242,6 +242,8 @@ hipError_t launch_fold(bool kda, int act_bf16, int state_bf16, int bv, bool mate
                        const FoldArgs& a, hipStream_t s);
 hipError_t launch_fold_fast(bool kda, int state_bf16, int bv, bool materialize,
                             const FoldArgs& a, const FoldFastLayout& lay, hipStream_t s);
+hipError_t launch_fold_bf16(bool kda, bool materialize, const FoldArgs& a,
+                            const FoldFastLayout& lay, hipStream_t s);
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
 
 }  // namespace rs

@@ -125,6 +125,15 @@ def test_bf16_state_history_and_fused_folds(T):
     _run(cfg)
 
 
+@pytest.mark.parametrize('policy', ['every_commit', 'none'])
+def test_kda_bf16_state(policy):
+    """KDA with a bf16 state: commit folds of every accepted window, or history replay
+    and in-verify folds, and the materialized state at the end."""
+    cfg = W.CONFIGS['c3'].with_(B=5, hk=3, hv=3, state_dtype='bf16', policy=policy,
+                                accept=('uniform', 0, 3), steps=10)
+    _run(cfg)
+
+
 def test_odd_shapes():
     """dk=dv=16 (one 16-wide tile), dv=48 (three 16-wide tiles), dk=64, ring == window."""
     _run(W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=16, dv=48, L=3, T=3, accept=('uniform', 0, 3),
