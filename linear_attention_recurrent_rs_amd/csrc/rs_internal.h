@@ -171,6 +171,12 @@ __host__ __device__ constexpr bool fast_bf16_mfma(bool kda, bool bf16_state, int
   return !kda && bf16_state && bv == 128 && tmax >= 2 && tmax <= 8;
 }
 
+// The fast verify's readout on bf16 MFMAs over a split fp32 state (high and low bf16
+// parts): GDN, an fp32 state, 64-column tiles, windows 3..4.
+__host__ __device__ constexpr bool fast_f32_split(bool kda, bool bf16_state, int bv, int tmax) {
+  return !kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4);
+}
+
 inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T, int L) {
   auto al = [](int x) { return (x + 15) & ~15; };
   const int dk = 128, vpp = readout_vpp(tmax), ks = kKeyStride;
@@ -196,7 +202,7 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
   // bf16 MFMA readout writes them after its last read of the history records, keys, scores
   // and readout vectors, so it reuses that region when it is large enough.
   const bool bfm = fast_bf16_mfma(kda, bf16_state, bv, tmax);
-  const bool all_vec = (bv == 64 && tmax >= 8) || bfm;
+  const bool all_vec = (bv == 64 && tmax >= 8) || bfm || fast_f32_split(kda, bf16_state, bv, tmax);
   const int red_bytes = al(4 * (all_vec ? l.nvec_pad : vpp) * bv * 4);
   if (bfm && o - l.hkeys >= red_bytes) {
     l.red = l.hkeys;

@@ -129,6 +129,21 @@ constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
 }
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 values (K entries 0..3 of an MFMA operand) split into bf16 parts, x = hi + lo
+// + e with |e| <= 2^-16 |x|: hi keeps the upper 16 bits (truncation), lo is the exact
+// remainder rounded to nearest even (one v_cvt_pk_bf16_f32 per pair).
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, s4& hi, s4& lo) {
+  const uint32_t w0 = __float_as_uint(x0), w1 = __float_as_uint(x1);
+  const uint32_t w2 = __float_as_uint(x2), w3 = __float_as_uint(x3);
+  hi = __builtin_bit_cast(s4, u2{(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)});
+  const f2 r01 = {x0 - __uint_as_float(w0 & 0xffff0000u), x1 - __uint_as_float(w1 & 0xffff0000u)};
+  const f2 r23 = {x2 - __uint_as_float(w2 & 0xffff0000u), x3 - __uint_as_float(w3 & 0xffff0000u)};
+  lo = __builtin_bit_cast(s4, u2{__builtin_bit_cast(uint32_t, __builtin_convertvector(r01, b2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(r23, b2))});
+}
 
 // Element p (0..7) of four rows' 8-column chunks (one per row, 4 dwords of bf16 pairs),
 // packed as four bf16 K entries (rows 0..3) of an MFMA operand.
@@ -159,6 +174,9 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   // state straight from its loaded bytes (step 8).  A 16-lane group loads whole 256-byte
   // rows (8 columns a lane); wave w holds rows 32w + 16j + 4g + i (g = lane / 16, i < 4).
   constexpr bool BF16_MFMA = fast_bf16_mfma(KDA, sizeof(ST) == 2, BV, TMAX);
+  // GDN with an fp32 state, 64-column tiles, windows 3-4: the same MFMA readout over the
+  // state split into high and low bf16 parts (two MFMAs per block; step 8)
+  constexpr bool F32_SPLIT = fast_f32_split(KDA, sizeof(ST) == 2, BV, TMAX);
   constexpr int NTILE = BF16_MFMA ? 8 : QPT * 4;          // tile load instructions
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Lane mapping.  Column quad fastest (cc = lane % CC) makes 16 consecutive lanes read
@@ -169,7 +187,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   // row segments).
   constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   constexpr int RL = 64 / CC;                            // row groups per wave
-  constexpr bool ADJ = !MFMA_READOUT && TMAX >= 3;
+  constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && TMAX >= 3;
   const int cc = ADJ ? lane / RL : tid % CC;
   const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
@@ -477,7 +495,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
   //   the history part, step 8.)
   const int NP = lay.nvec_pad;
-  if ((MFMA_READOUT || BF16_MFMA) && hrows > 0) {
+  if ((MFMA_READOUT || BF16_MFMA || F32_SPLIT) && hrows > 0) {
     constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -644,6 +662,53 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
         float* dst = red + (wave * NPd + m) * BV + 8 * lc;
         store4(dst, f4{D[0][e], D[1][e], D[2][e], D[3][e]});
         store4(dst + 4, f4{D[4][e], D[5][e], D[6][e], D[7][e]});
+      }
+    }
+    lds_barrier();
+    if (tid < BV) {
+      const float scale = fold ? 1.f : Gam;
+#pragma unroll
+      for (int m = 0; m < NV2; ++m) {
+        if (m < nvec) {
+          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
+                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
+          p *= scale * Gp[m >> 1];
+          if (hrows > 0) p += hist[m * BV + tid];
+          Pv[m] = p;
+        }
+      }
+    }
+  } else if constexpr (F32_SPLIT) {
+    // R_v = S^T x_v for the raw inputs x_v = xkq row v on bf16 MFMAs, S = hi + lo: lane l
+    // holds rows 16 wave + 64 j + 4 (l / 16) + i at columns 4 (l % 16) + p, so the four
+    // lane groups of a wave cover 16 consecutive rows (the K block of j); MFMA p takes
+    // column 4 n + p of the tile at B column n.  Lane l ends with vector 4 (l / 16) + e
+    // at column 4 (l % 16) + p in element e of accumulator p.
+    const int lc = lane & 15, lg = lane >> 4;
+    f4 D[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) D[p] = f4{0.f, 0.f, 0.f, 0.f};
+    const s4 zero4 = s4{0, 0, 0, 0};
+    const bool vok = lc < nvec;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const s4 xa = *reinterpret_cast<const s4*>(xkq + (vok ? lc : 0) * KS + 4 * (rg + RG * j));
+      const s4 av = vok ? xa : zero4;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        s4 bh, bl;
+        split4(s[j][0][p], s[j][1][p], s[j][2][p], s[j][3][p], bh, bl);
+        D[p] = mfma_bf16_16x16x16(av, bh, D[p]);
+        D[p] = mfma_bf16_16x16x16(av, bl, D[p]);
+      }
+    }
+    const int NPd = lay.nvec_pad;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * lg + e;
+      if (v < nvec) {
+        const int m = v < T ? 2 * v : 2 * (v - T) + 1;
+        store4(red + (wave * NPd + m) * BV + 4 * lc, f4{D[0][e], D[1][e], D[2][e], D[3][e]});
       }
     }
     lds_barrier();
