@@ -99,15 +99,16 @@ rs_status verify_impl(bool kda, const rs_dims* d, const int32_t* cu_seqlens, int
   a.B = d->batch; a.T = d->T; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
   a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
   a.nblocks = d->batch * d->hv * a.NV;
-  a.cu_seqlens = cu_seqlens; a.ntok = ntok;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate;
   a.state = state; a.ring_k = ring_k; a.ring_d = ring_d; a.ring_g = ring_g;
   a.cursor = cursor; a.slot_idx = slot_idx; a.out = out; a.write_pos_out = write_pos_out;
   a.group_counter = group_counter; a.lay = plan.lay;
+  const rs::RowWindows w{cu_seqlens, ntok};
   hipError_t e = plan.fast
-      ? rs::launch_verify_fast(kda, d->state_dtype == RS_BF16, bv, plan.tmax, a, plan.flay, stream)
+      ? rs::launch_verify_fast(kda, d->state_dtype == RS_BF16, bv, plan.tmax, a, plan.flay, w,
+                               stream)
       : rs::launch_verify(kda, d->act_dtype == RS_BF16, d->state_dtype == RS_BF16, bv, plan.tmax,
-                          a, stream);
+                          a, w, stream);
   return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
 }
 

@@ -30,10 +30,6 @@ struct LdsLayout {
 
 struct VerifyArgs {
   int B, T, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
-  // ragged windows: row r verifies tokens [cu_seqlens[r], cu_seqlens[r + 1]) of ntok
-  // packed tokens (at most T of them); NULL = every row T tokens at r * T
-  const int32_t* cu_seqlens;
-  int ntok;
   const void* q;
   const void* k;
   const void* v;
@@ -51,6 +47,14 @@ struct VerifyArgs {
   LdsLayout lay;
 };
 
+// Ragged windows: row r verifies tokens [cu_seqlens[r], cu_seqlens[r + 1]) of ntok packed
+// tokens (at most T of them); cu_seqlens NULL = every row T tokens at r * T.  The verify
+// kernels take it as their last argument, so that the other arguments keep their offsets.
+struct RowWindows {
+  const int32_t* cu_seqlens;
+  int ntok;
+};
+
 struct FoldArgs {
   int B, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
   const void* state_in;     // S (read)
@@ -65,13 +69,13 @@ struct FoldArgs {
 
 struct AdvanceArgs {
   int B, T, L, num_slots, policy, next_T;
-  const int32_t* cu_seqlens;   // ragged windows as in VerifyArgs, or NULL
-  int ntok;
   int32_t* cursor;
   int32_t* fold_len;
   const int32_t* slot_idx;
   const int32_t* accept;
   const uint8_t* force_mask;
+  const int32_t* cu_seqlens;   // ragged windows as in VerifyArgs, or NULL
+  int ntok;
 };
 
 // The verify window of a request row: its first token and its width.  Uniform windows
@@ -241,9 +245,9 @@ inline FoldFastLayout fold_fast_layout(bool kda, int bv, int L) {
 
 // Launchers (defined in rs_kernels.hip, rs_verify_fast.hip and rs_fold_fast.hip).  Return hipGetLastError() after the launch.
 hipError_t launch_verify(bool kda, int act_bf16, int state_bf16, int bv, int tmax,
-                         const VerifyArgs& a, hipStream_t s);
+                         const VerifyArgs& a, const RowWindows& w, hipStream_t s);
 hipError_t launch_verify_fast(bool kda, int state_bf16, int bv, int tmax, const VerifyArgs& a,
-                              const FastLayout& lay, hipStream_t s);
+                              const FastLayout& lay, const RowWindows& w, hipStream_t s);
 hipError_t launch_fold(bool kda, int act_bf16, int state_bf16, int bv, bool materialize,
                        const FoldArgs& a, hipStream_t s);
 hipError_t launch_fold_fast(bool kda, int state_bf16, int bv, bool materialize,

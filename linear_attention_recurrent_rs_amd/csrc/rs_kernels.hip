@@ -184,7 +184,7 @@ __device__ __forceinline__ void readout(const ET* tile, const float* xs, int xs_
 
 // ------------------------------------------------------------------ verify
 template <bool KDA, typename AT, typename ST, int BV, int TMAX>
-__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a, RowWindows rw) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int VPP = (2 * TMAX < 8) ? 2 * TMAX : 8;
   const int tid = threadIdx.x;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
   const int kh = h / a.G, col0 = vt * BV;
   int T;
   size_t tok0;
-  row_window(a.cu_seqlens, a.ntok, a.T, row, &T, &tok0);
+  row_window(rw.cu_seqlens, rw.ntok, a.T, row, &T, &tok0);
   int n = a.cursor[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   const bool fold = n + T > L;                           // the window would overflow
@@ -457,51 +457,51 @@ static void set_lds_limit(K kernel, int bytes) {
 }
 
 template <bool KDA, typename AT, typename ST, int BV, int TMAX>
-static hipError_t run_verify(const VerifyArgs& a, hipStream_t s) {
+static hipError_t run_verify(const VerifyArgs& a, const RowWindows& w, hipStream_t s) {
   auto k = verify_kernel<KDA, AT, ST, BV, TMAX>;
   set_lds_limit(k, a.lay.total);
-  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), a.lay.total, s, a);
+  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), a.lay.total, s, a, w);
   return hipGetLastError();
 }
 
 template <bool KDA, typename AT, typename ST, int BV>
-static hipError_t verify_tmax(int tmax, const VerifyArgs& a, hipStream_t s) {
+static hipError_t verify_tmax(int tmax, const VerifyArgs& a, const RowWindows& w, hipStream_t s) {
   switch (tmax) {
-    case 1: return run_verify<KDA, AT, ST, BV, 1>(a, s);
-    case 2: return run_verify<KDA, AT, ST, BV, 2>(a, s);
-    case 4: return run_verify<KDA, AT, ST, BV, 4>(a, s);
-    case 8: return run_verify<KDA, AT, ST, BV, 8>(a, s);
-    case 16: return run_verify<KDA, AT, ST, BV, 16>(a, s);
+    case 1: return run_verify<KDA, AT, ST, BV, 1>(a, w, s);
+    case 2: return run_verify<KDA, AT, ST, BV, 2>(a, w, s);
+    case 4: return run_verify<KDA, AT, ST, BV, 4>(a, w, s);
+    case 8: return run_verify<KDA, AT, ST, BV, 8>(a, w, s);
+    case 16: return run_verify<KDA, AT, ST, BV, 16>(a, w, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool KDA, typename AT, typename ST>
-static hipError_t verify_bv(int bv, int tmax, const VerifyArgs& a, hipStream_t s) {
+static hipError_t verify_bv(int bv, int tmax, const VerifyArgs& a, const RowWindows& w, hipStream_t s) {
   switch (bv) {
-    case 16: return verify_tmax<KDA, AT, ST, 16>(tmax, a, s);
-    case 32: return verify_tmax<KDA, AT, ST, 32>(tmax, a, s);
-    case 64: return verify_tmax<KDA, AT, ST, 64>(tmax, a, s);
-    case 128: return verify_tmax<KDA, AT, ST, 128>(tmax, a, s);
+    case 16: return verify_tmax<KDA, AT, ST, 16>(tmax, a, w, s);
+    case 32: return verify_tmax<KDA, AT, ST, 32>(tmax, a, w, s);
+    case 64: return verify_tmax<KDA, AT, ST, 64>(tmax, a, w, s);
+    case 128: return verify_tmax<KDA, AT, ST, 128>(tmax, a, w, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool KDA>
 static hipError_t verify_types(int act_bf16, int state_bf16, int bv, int tmax,
-                               const VerifyArgs& a, hipStream_t s) {
+                               const VerifyArgs& a, const RowWindows& w, hipStream_t s) {
   if (act_bf16) {
-    return state_bf16 ? verify_bv<KDA, bf16, bf16>(bv, tmax, a, s)
-                      : verify_bv<KDA, bf16, float>(bv, tmax, a, s);
+    return state_bf16 ? verify_bv<KDA, bf16, bf16>(bv, tmax, a, w, s)
+                      : verify_bv<KDA, bf16, float>(bv, tmax, a, w, s);
   }
-  return state_bf16 ? verify_bv<KDA, float, bf16>(bv, tmax, a, s)
-                    : verify_bv<KDA, float, float>(bv, tmax, a, s);
+  return state_bf16 ? verify_bv<KDA, float, bf16>(bv, tmax, a, w, s)
+                    : verify_bv<KDA, float, float>(bv, tmax, a, w, s);
 }
 
 hipError_t launch_verify(bool kda, int act_bf16, int state_bf16, int bv, int tmax,
-                         const VerifyArgs& a, hipStream_t s) {
-  return kda ? verify_types<true>(act_bf16, state_bf16, bv, tmax, a, s)
-             : verify_types<false>(act_bf16, state_bf16, bv, tmax, a, s);
+                         const VerifyArgs& a, const RowWindows& w, hipStream_t s) {
+  return kda ? verify_types<true>(act_bf16, state_bf16, bv, tmax, a, w, s)
+             : verify_types<false>(act_bf16, state_bf16, bv, tmax, a, w, s);
 }
 
 template <bool KDA, typename AT, typename ST, int BV, bool MAT>

@@ -154,9 +154,11 @@ __device__ __forceinline__ s4 column_of(const u4 (&r)[4], int p) {
   return __builtin_bit_cast(s4, u2{e0 | (e1 << 16), e2 | (e3 << 16)});
 }
 
-template <bool KDA, typename ST, int BV, int TMAX>
+// RAGGED: windows from cumulative lengths (a separate instantiation, so that the uniform
+// kernel carries none of its code).
+template <bool KDA, typename ST, int BV, int TMAX, bool RAGGED>
 __global__ __launch_bounds__(kThreads, fast_min_blocks(KDA, BV, TMAX, sizeof(ST) == 2))
-void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
+void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   constexpr int DK = 128, KS = kKeyStride;
   // Tile split: thread (rg, cc) holds rows 4*(rg + RG*j) + i (j < QPT, i < 4) of column
   // quad cc, so that each load instruction of a wave covers whole 256-byte row segments
@@ -201,7 +203,10 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   const int kh = h / a.G, col0 = vt * BV;
   int T;
   size_t tok0;
-  row_window(a.cu_seqlens, a.ntok, a.T, row, &T, &tok0);
+  // uniform decode (TMAX = 1) has T = 1 at compile time; every other window is read at run
+  // time (a compile-time window of 2-4 would spill under the register caps above)
+  row_window(RAGGED ? rw.cu_seqlens : nullptr, rw.ntok, (!RAGGED && TMAX == 1) ? 1 : a.T, row,
+             &T, &tok0);
   const int XS = lay.xs_stride, CS = lay.cs;
 
   bf16* xkq = reinterpret_cast<bf16*>(smem + lay.xkq);
@@ -235,7 +240,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
   const bool fold = n + T > L;                           // the window would overflow
   const int base = fold ? 0 : n;                         // write_pos
   const int nh = n;
-  if (T == 0) {                                          // an empty ragged window
+  if (RAGGED && T == 0) {                                // an empty ragged window
     if (a.write_pos_out && h == 0 && vt == 0 && tid == 0) a.write_pos_out[row] = base;
     return;
   }
@@ -908,45 +913,48 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay) {
 }
 
 template <bool KDA, typename ST, int BV, int TMAX>
-static hipError_t run_fast(const VerifyArgs& a, const FastLayout& lay, hipStream_t s) {
-  auto k = verify_fast_kernel<KDA, ST, BV, TMAX>;
+static hipError_t run_fast(const VerifyArgs& a, const FastLayout& lay, const RowWindows& w,
+                           hipStream_t s) {
+  auto k = w.cu_seqlens ? verify_fast_kernel<KDA, ST, BV, TMAX, true>
+                        : verify_fast_kernel<KDA, ST, BV, TMAX, false>;
   if (lay.total > 65536)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lay.total);
-  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), lay.total, s, a, lay);
+  hipLaunchKernelGGL(k, dim3(a.nblocks), dim3(kThreads), lay.total, s, a, lay, w);
   return hipGetLastError();
 }
 
 template <bool KDA, typename ST, int BV>
-static hipError_t fast_tmax(int tmax, const VerifyArgs& a, const FastLayout& lay, hipStream_t s) {
+static hipError_t fast_tmax(int tmax, const VerifyArgs& a, const FastLayout& lay,
+                            const RowWindows& w, hipStream_t s) {
   switch (tmax) {
-    case 1: return run_fast<KDA, ST, BV, 1>(a, lay, s);
-    case 2: return run_fast<KDA, ST, BV, 2>(a, lay, s);
-    case 3: return run_fast<KDA, ST, BV, 3>(a, lay, s);
-    case 4: return run_fast<KDA, ST, BV, 4>(a, lay, s);
-    case 8: return run_fast<KDA, ST, BV, 8>(a, lay, s);
-    case 16: return run_fast<KDA, ST, BV, 16>(a, lay, s);
+    case 1: return run_fast<KDA, ST, BV, 1>(a, lay, w, s);
+    case 2: return run_fast<KDA, ST, BV, 2>(a, lay, w, s);
+    case 3: return run_fast<KDA, ST, BV, 3>(a, lay, w, s);
+    case 4: return run_fast<KDA, ST, BV, 4>(a, lay, w, s);
+    case 8: return run_fast<KDA, ST, BV, 8>(a, lay, w, s);
+    case 16: return run_fast<KDA, ST, BV, 16>(a, lay, w, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool KDA, typename ST>
 static hipError_t fast_bv(int bv, int tmax, const VerifyArgs& a, const FastLayout& lay,
-                          hipStream_t s) {
+                          const RowWindows& w, hipStream_t s) {
   switch (bv) {
-    case 32: return fast_tmax<KDA, ST, 32>(tmax, a, lay, s);
-    case 64: return fast_tmax<KDA, ST, 64>(tmax, a, lay, s);
-    case 128: return fast_tmax<KDA, ST, 128>(tmax, a, lay, s);
+    case 32: return fast_tmax<KDA, ST, 32>(tmax, a, lay, w, s);
+    case 64: return fast_tmax<KDA, ST, 64>(tmax, a, lay, w, s);
+    case 128: return fast_tmax<KDA, ST, 128>(tmax, a, lay, w, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_verify_fast(bool kda, int state_bf16, int bv, int tmax, const VerifyArgs& a,
-                              const FastLayout& lay, hipStream_t s) {
-  if (kda) return state_bf16 ? fast_bv<true, bf16>(bv, tmax, a, lay, s)
-                             : fast_bv<true, float>(bv, tmax, a, lay, s);
-  return state_bf16 ? fast_bv<false, bf16>(bv, tmax, a, lay, s)
-                    : fast_bv<false, float>(bv, tmax, a, lay, s);
+                              const FastLayout& lay, const RowWindows& w, hipStream_t s) {
+  if (kda) return state_bf16 ? fast_bv<true, bf16>(bv, tmax, a, lay, w, s)
+                             : fast_bv<true, float>(bv, tmax, a, lay, w, s);
+  return state_bf16 ? fast_bv<false, bf16>(bv, tmax, a, lay, w, s)
+                    : fast_bv<false, float>(bv, tmax, a, lay, w, s);
 }
 
 }  // namespace rs
