@@ -151,7 +151,7 @@ struct FastLayout {
   int hd;       // history deltas of this tile, fp32 [L x bv]       (HBM -> LDS copy)
   int hg;       // history gates, fp32 [L] (GDN) or [L x 128] (KDA) (HBM -> LDS copy)
   int gam_i;    // GDN: suffix decay of each history record, fp32 [L]
-  int khat;     // KDA: keys times their suffix decay, fp32 [L x xs_stride]
+  int khat;     // KDA: keys times their suffix decay, fp32 [L x 128], in place of hg
   int Gam;      // KDA: total history decay per key channel, fp32 [128]
   int xs;       // KDA: window vectors times the in-window prefix decay [2*tmax x xs_stride]
   int xr;       // readout vectors, q_t and k_t interleaved [nvec_pad x xs_stride]
@@ -190,28 +190,51 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
   l.nvec_pad = ((2 * T + vpp - 1) / vpp) * vpp;
   l.cs = (2 * tmax + 15) & ~15;
   l.lp = (L + 15) & ~15;
-  l.xkq = o; o += al(2 * tmax * ks * 2);
-  l.xv = o; o += al(tmax * bv * 2);
-  l.xg = o; o += kda ? al(tmax * ks * 2) : 0;
-  l.hkeys = o; o += al(L * ks * 2);
-  l.hd = o; o += al(L * bv * 4);
-  l.hg = o; o += al(kda ? L * dk * 4 : L * 4);
-  l.gam_i = o; o += kda ? 0 : al(L * 4);
-  l.khat = o; o += kda ? al(L * l.xs_stride * 4) : 0;
-  l.Gam = o; o += kda ? al(dk * 4) : 0;
-  l.xs = o; o += kda ? al(2 * tmax * l.xs_stride * 4) : 0;
-  l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
-  l.C = o; o += al((kda ? 4 : 1) * l.lp * l.cs * 4);
-  // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readouts).  The
-  // bf16 MFMA readout writes them after its last read of the history records, keys, scores
-  // and readout vectors, so it reuses that region when it is large enough.
   const bool bfm = fast_bf16_mfma(kda, bf16_state, bv, tmax);
   const bool all_vec = (bv == 64 && tmax >= 8) || bfm || fast_f32_split(kda, bf16_state, bv, tmax);
   const int red_bytes = al(4 * (all_vec ? l.nvec_pad : vpp) * bv * 4);
-  if (bfm && o - l.hkeys >= red_bytes) {
-    l.red = l.hkeys;
+  l.xkq = o; o += al(2 * tmax * ks * 2);
+  l.xv = o; o += al(tmax * bv * 2);
+  if (kda) {
+    // KDA: the decayed history keys replace the history gates in place (rows of 128); the
+    // raw history keys and the decayed window vectors are dead once the scores are formed,
+    // so the readout partials reuse them when they fit
+    l.xg = o; o += al(tmax * ks * 2);
+    l.hd = o; o += al(L * bv * 4);
+    l.hg = o; o += al(L * dk * 4);
+    l.khat = l.hg;
+    l.gam_i = o;
+    l.Gam = o; o += al(dk * 4);
+    const int dead = o;
+    l.hkeys = o; o += al(L * ks * 2);
+    l.xs = o; o += al(2 * tmax * l.xs_stride * 4);
+    const int dead_end = o;
+    l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
+    l.C = o; o += al(4 * l.lp * l.cs * 4);
+    if (dead_end - dead >= red_bytes) {
+      l.red = dead;
+    } else {
+      l.red = o; o += red_bytes;
+    }
   } else {
-    l.red = o; o += red_bytes;
+    l.xg = o;
+    l.hkeys = o; o += al(L * ks * 2);
+    l.hd = o; o += al(L * bv * 4);
+    l.hg = o; o += al(L * 4);
+    l.gam_i = o; o += al(L * 4);
+    l.khat = o;
+    l.Gam = o;
+    l.xs = o;
+    l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
+    l.C = o; o += al(l.lp * l.cs * 4);
+    // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readouts).  The
+    // bf16 MFMA readout writes them after its last read of the history records, keys, scores
+    // and readout vectors, so it reuses that region when it is large enough.
+    if (bfm && o - l.hkeys >= red_bytes) {
+      l.red = l.hkeys;
+    } else {
+      l.red = o; o += red_bytes;
+    }
   }
   l.hist = o; o += all_vec ? al(l.nvec_pad * bv * 4) : 0;
   l.Am = o; o += al(tmax * tmax * 4);

@@ -378,9 +378,10 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         xs[(T + t) * XS + tid] = k;
       }
       float g = 1.f;
-      for (int i = nh - 1; i >= 0; --i) {
-        khat[i * XS + tid] = g * to_f32(hkeys[i * KS + tid]);
-        g *= hg[i * DK + tid];
+      for (int i = nh - 1; i >= 0; --i) {            // khat replaces the gates in place
+        const float al = hg[i * DK + tid];
+        khat[i * DK + tid] = g * to_f32(hkeys[i * KS + tid]);
+        g *= al;
       }
       Gamv[tid] = g;
       const float scale = fold ? 1.f : g;
@@ -448,7 +449,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       const int rt = CT == 1 ? tile : tile >> 1, ct = CT == 1 ? 0 : tile & 1;
       const int ra = rt * 16 + l16, m = ct * 16 + l16;
       const bool aok = ra < hrows, bok = m < nvec;
-      const float* ap = khat + (aok ? ra : 0) * XS;
+      const float* ap = khat + (aok ? ra : 0) * DK;
       const float* bp = xs + (bok ? m : 0) * XS;
       float av[8], bv[8];
 #pragma unroll
@@ -609,7 +610,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
         const int r0 = 4 * (rg + RG * j);
-        const f4 kq = KDA ? load4(khat + i * XS + r0) : bf16x4(hkeys + i * KS + r0);
+        const f4 kq = KDA ? load4(khat + i * DK + r0) : bf16x4(hkeys + i * KS + r0);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) s[j][ii] += kq[ii] * dq;
       }
