@@ -176,9 +176,11 @@ __host__ __device__ constexpr bool fast_bf16_mfma(bool kda, bool bf16_state, int
 }
 
 // The fast verify's readout on bf16 MFMAs over a split fp32 state (high and low bf16
-// parts): GDN, an fp32 state, 64-column tiles, windows 3..4.
+// parts): GDN, an fp32 state, 64-column tiles, windows 3..4 and 5..8 (at most 16 readout
+// vectors).  At 5..8 it also needs no fp32 readout vectors in LDS, and its partials reuse
+// the history region.
 __host__ __device__ constexpr bool fast_f32_split(bool kda, bool bf16_state, int bv, int tmax) {
-  return !kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4);
+  return !kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4 || tmax == 8);
 }
 
 inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T, int L) {
@@ -225,12 +227,14 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
     l.khat = o;
     l.Gam = o;
     l.xs = o;
-    l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
+    const bool split8 = fast_f32_split(kda, bf16_state, bv, tmax) && tmax == 8;
+    l.xr = o; o += split8 ? 0 : al(l.nvec_pad * l.xs_stride * 4);
     l.C = o; o += al(l.lp * l.cs * 4);
     // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readouts).  The
-    // bf16 MFMA readout writes them after its last read of the history records, keys, scores
-    // and readout vectors, so it reuses that region when it is large enough.
-    if (bfm && o - l.hkeys >= red_bytes) {
+    // bf16 MFMA readouts of a bf16 state and of a split fp32 state at windows 5..8 write
+    // them after their last read of the history records, keys and scores (behind a
+    // barrier), so they reuse that region when it is large enough.
+    if ((bfm || split8) && o - l.hkeys >= red_bytes) {
       l.red = l.hkeys;
     } else {
       l.red = o; o += red_bytes;

@@ -338,14 +338,16 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         xk[t] = to_f32(xkq[(T + t) * KS + tid]);
       }
       const float scale = fold ? 1.f : Gam;
+      if constexpr (!(F32_SPLIT && TMAX == 8)) {         // (no fp32 readout vectors there)
 #pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-          xr[(2 * t) * XS + tid] = (scale * Gp[t]) * xq[t];
-          xr[(2 * t + 1) * XS + tid] = (scale * Gp[t]) * xk[t];
+        for (int t = 0; t < TMAX; ++t) {
+          if (t < T) {
+            xr[(2 * t) * XS + tid] = (scale * Gp[t]) * xq[t];
+            xr[(2 * t + 1) * XS + tid] = (scale * Gp[t]) * xk[t];
+          }
         }
+        for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
       }
-      for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
     } else if (wave == 2 && L > 16) {
       // gamma_i = prod_{i<j<nh} alpha_j: an inclusive suffix product over the lanes of
       // one wave, shifted by one lane (rings up to 64 records; longer rings loop)
@@ -709,6 +711,9 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     const int NPd = lay.nvec_pad;
+    // windows 5..8: the partials reuse the history region, which every wave has finished
+    // reading here
+    if constexpr (TMAX == 8) lds_barrier();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int v = 4 * lg + e;
