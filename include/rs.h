@@ -220,6 +220,32 @@ rs_status rs_materialize(const rs_dims* dims, int is_kda, const void* state,
                          const int32_t* cursor, const int32_t* slot_idx, float* out_state,
                          hipStream_t stream);
 
+/*
+ * rs_snapshot_verify, rs_snapshot_commit -- the snapshot-verify baseline that ReplaySSM
+ * replaces, for comparison in time and memory (sglang PR, Behavior changes and Speed
+ * Tests: the snapshot verify writes one full state per draft token, 72.6 GB against
+ * 3.04 GB of ring at TP1 with 128 requests, and the commit scatters the accepted
+ * snapshot).  No ring and no cursor: the verify runs the recurrence token by token from
+ * S[slot] and writes S after every draft token; the commit copies the accepted one back.
+ *   is_kda      0 = GDN (gate [B*T, hv]), 1 = KDA (hv == hk, gate [B*T, hv, dk])
+ *   q, k, v, beta, gate, out   as for rs_gdn_verify / rs_kda_verify
+ *   state       [num_slots, hv, dk, dv] state dtype; read by the verify, written by the
+ *               commit (slot of each live row with accept_len > 0)
+ *   snapshots   [B, T, hv, dk, dv] state dtype: snapshots[r, t] = S after draft t of row r
+ *               (bf16: round-to-nearest-even); caller-owned, written by the verify
+ *   accept_len  [B] int32 in [0, T]; 0 leaves the state as it is
+ * Null rows (slot < 0) are skipped by both.  dims->ring_cap must still be >= T (the
+ * dims are shared with the ring calls); dims->tile_v = 0 or a width up to 64.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_LAUNCH.
+ */
+rs_status rs_snapshot_verify(const rs_dims* dims, int is_kda, const void* q, const void* k,
+                             const void* v, const void* beta, const void* gate,
+                             const void* state, void* snapshots, const int32_t* slot_idx,
+                             float* out, hipStream_t stream);
+rs_status rs_snapshot_commit(const rs_dims* dims, void* state, const void* snapshots,
+                             const int32_t* slot_idx, const int32_t* accept_len,
+                             hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* rs_status_str(rs_status status);
 

@@ -18,6 +18,7 @@ import torch
 
 __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'commit_fold',
            'gdn_verify_varlen', 'kda_verify_varlen', 'cursor_advance_varlen',
+           'snapshot_verify', 'snapshot_commit',
            'prepare_verify_varlen', 'prepare_cursor_advance_varlen',
            'materialize', 'verify_launch_info', 'stream_read', 'library_path', 'F32', 'BF16',
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
@@ -77,6 +78,10 @@ def _lib():
         lib.rs_commit_fold.restype = ctypes.c_int
         lib.rs_materialize.argtypes = [dp, ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P]
         lib.rs_materialize.restype = ctypes.c_int
+        lib.rs_snapshot_verify.argtypes = [dp, ctypes.c_int] + [_P] * 10
+        lib.rs_snapshot_verify.restype = ctypes.c_int
+        lib.rs_snapshot_commit.argtypes = [dp] + [_P] * 5
+        lib.rs_snapshot_commit.restype = ctypes.c_int
         lib.rs_status_str.argtypes = [ctypes.c_int]
         lib.rs_status_str.restype = ctypes.c_char_p
         lib.rs_verify_launch_info.argtypes = [dp, ctypes.c_int, _P, _P, _P]
@@ -250,6 +255,35 @@ def materialize(d: Dims, kda: bool, state, ring_k, ring_d, ring_g, cursor, slot_
                                  _ptr(out_state, 'out_state', d.batch * d.hv * d.dk * d.dv,
                                       torch.float32),
                                  _stream(stream)), 'rs_materialize')
+
+
+def snapshot_verify(d: Dims, kda: bool, q, k, v, beta, gate, state, snapshots, slot_idx, out,
+                    stream=None):
+    """rs_snapshot_verify: the snapshot-verify baseline; snapshots [B, T, hv, dk, dv] in the
+    state dtype receive S after every draft token."""
+    at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
+    BT = d.batch * d.T
+    g_per = d.hv * d.dk if kda else d.hv
+    args = [_ptr(q, 'q', BT * d.hk * d.dk, at), _ptr(k, 'k', BT * d.hk * d.dk, at),
+            _ptr(v, 'v', BT * d.hv * d.dv, at), _ptr(beta, 'beta', BT * d.hv, at),
+            _ptr(gate, 'gate', BT * g_per, at),
+            _ptr(state, 'state', d.num_slots * d.hv * d.dk * d.dv, st),
+            _ptr(snapshots, 'snapshots', BT * d.hv * d.dk * d.dv, st),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(out, 'out', BT * d.hv * d.dv, torch.float32)]
+    _check(_lib().rs_snapshot_verify(ctypes.byref(d), int(kda), *args, _stream(stream)),
+           'rs_snapshot_verify')
+
+
+def snapshot_commit(d: Dims, state, snapshots, slot_idx, accept_len, stream=None):
+    """rs_snapshot_commit: state[slot] <- snapshots[row, accept - 1] for accept > 0."""
+    st = _TORCH_DTYPE[d.state_dtype]
+    args = [_ptr(state, 'state', d.num_slots * d.hv * d.dk * d.dv, st),
+            _ptr(snapshots, 'snapshots', d.batch * d.T * d.hv * d.dk * d.dv, st),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    _check(_lib().rs_snapshot_commit(ctypes.byref(d), *args, _stream(stream)),
+           'rs_snapshot_commit')
 
 
 def verify_launch_info(d: Dims, kda: bool = False):

@@ -24,7 +24,8 @@ DEVICE_FLAGS = ['-Xclang', '-target-feature', '-Xclang', '-packed-fp32-ops']
 COMMON = ['-O3', '-fPIC', '-std=c++17', f'--offload-arch={ARCH}', '-mcode-object-version=5',
           '-I', os.path.join(ROOT, 'include'), '-I', CSRC, '-Wall', '-Wno-unused-function']
 
-SOURCES = ['rs_kernels.hip', 'rs_verify_fast.hip', 'rs_fold_fast.hip', 'rs_probe.hip', 'rs_api.cpp']
+SOURCES = ['rs_kernels.hip', 'rs_verify_fast.hip', 'rs_fold_fast.hip', 'rs_snapshot.hip',
+           'rs_probe.hip', 'rs_api.cpp']
 
 
 def _compile(src: str) -> str:

@@ -2,6 +2,7 @@
 // Every entry point enqueues on the caller's stream and returns without synchronising.
 #include "rs.h"
 #include "rs_internal.h"
+#include "rs_snapshot.h"
 
 namespace {
 
@@ -273,6 +274,44 @@ rs_status rs_materialize(const rs_dims* dims, int is_kda, const void* state, con
   if (out_state == nullptr && dims && dims->batch > 0) return RS_E_NULLPTR;
   return fold_impl(dims, is_kda, state, out_state, ring_k, ring_d, ring_g, cursor, slot_idx,
                    true, stream);
+}
+
+rs_status rs_snapshot_verify(const rs_dims* dims, int is_kda, const void* q, const void* k,
+                             const void* v, const void* beta, const void* gate,
+                             const void* state, void* snapshots, const int32_t* slot_idx,
+                             float* out, hipStream_t stream) {
+  rs_status st = check_common(dims, true);
+  if (st != RS_OK) return st;
+  const bool kda = is_kda != 0;
+  if (kda && dims->hv != dims->hk) return RS_E_SHAPE;
+  int bv = dims->tile_v ? dims->tile_v : (dims->dv % 64 == 0 ? 64 : dims->dv % 32 == 0 ? 32 : 16);
+  if (bv > 64) bv = 64;
+  if (dims->dv % bv != 0 || rs::snapshot_lds_bytes(dims->dk, bv) > kMaxLds) return RS_E_SHAPE;
+  if (dims->batch == 0) return RS_OK;
+  if (!q || !k || !v || !beta || !gate || !state || !snapshots || !slot_idx || !out)
+    return RS_E_NULLPTR;
+  rs::SnapArgs a{};
+  a.B = dims->batch; a.T = dims->T; a.hk = dims->hk; a.hv = dims->hv; a.dk = dims->dk;
+  a.dv = dims->dv; a.G = dims->hv / dims->hk; a.NV = dims->dv / bv;
+  a.nblocks = dims->batch * dims->hv * a.NV; a.num_slots = dims->num_slots;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate; a.state = state;
+  a.snapshots = snapshots; a.slot_idx = slot_idx; a.out = out;
+  return rs::launch_snapshot_verify(kda, dims->act_dtype == RS_BF16, dims->state_dtype == RS_BF16,
+                                    bv, a, stream) == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+rs_status rs_snapshot_commit(const rs_dims* dims, void* state, const void* snapshots,
+                             const int32_t* slot_idx, const int32_t* accept_len,
+                             hipStream_t stream) {
+  rs_status st = check_common(dims, true);
+  if (st != RS_OK) return st;
+  if (dims->batch == 0) return RS_OK;
+  if (!state || !snapshots || !slot_idx || !accept_len) return RS_E_NULLPTR;
+  rs::SnapCommitArgs a{};
+  a.B = dims->batch; a.T = dims->T; a.hv = dims->hv; a.dk = dims->dk; a.dv = dims->dv;
+  a.num_slots = dims->num_slots; a.elem_bytes = dbytes(dims->state_dtype);
+  a.state = state; a.snapshots = snapshots; a.slot_idx = slot_idx; a.accept = accept_len;
+  return rs::launch_snapshot_commit(a, stream) == hipSuccess ? RS_OK : RS_E_LAUNCH;
 }
 
 const char* rs_status_str(rs_status s) {

@@ -220,6 +220,11 @@ class TokenStream:
             self._window[s] = states
         return out, dels
 
+    def window_state(self, s: int, t: int) -> np.ndarray:
+        """The state after draft token t of slot s's last verify: what the snapshot-verify
+        baseline keeps per draft token (sglang PR, the snapshot verify it replaces)."""
+        return self._window[s][t]
+
     def accept(self, slots, accept, rows=None):
         for r in _rows(slots, rows):
             s = int(slots[r])

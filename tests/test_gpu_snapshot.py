@@ -1,0 +1,121 @@
+"""GPU parity of the snapshot-verify baseline (rs_snapshot_verify / rs_snapshot_commit)
+against the fp64 token-stream definition, through the C ABI.
+
+The snapshot verify runs the recurrence token by token from the slot's state and writes
+the state after every draft token; the commit copies the accepted one back.  Checked per
+step (bf16 states: with the definition restarted each step from the committed bf16 state,
+since this baseline rounds every snapshot and every commit): outputs and every snapshot against the definition's states after each draft token
+(at positions where the definition is finite), the committed state bit for bit equal to
+the accepted snapshot, null rows and unused slots untouched, and the ReplaySSM verify of
+the same workload giving the same outputs within tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import replay as rp
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_inputs(cfg, inp):
+    BT = cfg.B * cfg.T
+    gsh = (BT, cfg.hv, cfg.dk) if cfg.kda else (BT, cfg.hv)
+    return (H.to_dev(inp.q.reshape(BT, cfg.hk, cfg.dk), cfg.act_dtype, 'cuda'),
+            H.to_dev(inp.k.reshape(BT, cfg.hk, cfg.dk), cfg.act_dtype, 'cuda'),
+            H.to_dev(inp.v.reshape(BT, cfg.hv, cfg.dv), cfg.act_dtype, 'cuda'),
+            H.to_dev(inp.beta.reshape(BT, cfg.hv), cfg.act_dtype, 'cuda'),
+            H.to_dev(inp.gate.reshape(gsh), cfg.act_dtype, 'cuda'))
+
+
+def _run_snapshot(cfg, steps):
+    import linear_attention_recurrent_rs_amd as rs
+    init = H.initial(cfg)
+    slots = init.slots
+    live = [r for r in range(cfg.B) if slots[r] >= 0]
+    tol = H.tol_for(cfg)
+    d = rs.Dims(cfg.B, cfg.T, cfg.hk, cfg.hv, cfg.dk, cfg.dv, cfg.L, cfg.num_slots,
+                rs.BF16 if cfg.act_dtype == 'bf16' else rs.F32,
+                rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, 0)
+    sdt = H.torch_dtype(cfg.state_dtype)
+    S = H.to_dev(init.S[0], cfg.state_dtype, 'cuda')
+    S_init = S.clone()
+    snaps = torch.full((cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv), 7.0, dtype=sdt, device='cuda')
+    out = torch.full((cfg.B * cfg.T, cfg.hv, cfg.dv), H.SENTINEL_OUT, device='cuda')
+    slot_d = torch.from_numpy(slots.astype(np.int32)).cuda()
+    ts = rp.TokenStream({int(slots[r]): init.S[0][slots[r]] for r in live}, cfg.kda, cfg.G)
+    worst = 0.0
+    for j in range(steps):
+        acc, ins, _, _ = H.step_data(cfg, j)
+        print(f'[{cfg.name} snapshot] step {j}', flush=True)
+        rs.snapshot_verify(d, cfg.kda, *_dev_inputs(cfg, ins[0]), S, snaps, slot_d, out)
+        o_ref, _ = ts.verify(slots, ins[0])
+        o_gpu = out.cpu().numpy().reshape(cfg.B, cfg.T, cfg.hv, cfg.dv)
+        sn = snaps.float().cpu().numpy()
+        for r in range(cfg.B):
+            if slots[r] < 0:
+                assert np.all(o_gpu[r] == H.SENTINEL_OUT) and np.all(sn[r] == 7.0), 'null row written'
+                continue
+            s = int(slots[r])
+            fin = np.isfinite(o_ref[r])
+            assert np.all(fin[:acc[r]]) and np.all(np.isfinite(o_gpu[r, :acc[r]]))
+            worst = max(worst, H.rel_err(o_gpu[r][fin], o_ref[r][fin]))
+            for t in range(cfg.T):
+                ref = ts.window_state(s, t)
+                if np.all(np.isfinite(ref)):
+                    worst = max(worst, H.rel_err(sn[r, t], ref))
+        before = S.clone()
+        rs.snapshot_commit(d, S, snaps, slot_d, torch.from_numpy(acc.astype(np.int32)).cuda())
+        ts.accept(slots, acc)
+        for r in live:
+            s = int(slots[r])
+            if acc[r] > 0:
+                assert torch.equal(S[s], snaps[r, acc[r] - 1]), 'commit is not the accepted snapshot'
+            else:
+                assert torch.equal(S[s], before[s]), 'a zero accept changed the state'
+            worst = max(worst, H.rel_err(S[s].float().cpu().numpy(), ts.H[s]))
+        assert worst <= tol, f'snapshot baseline error {worst:.3e} > {tol}'
+        if cfg.state_dtype == 'bf16':
+            # teacher forcing: the next step of the definition starts from the committed
+            # bf16 state, so each step is held to one rounding plus its arithmetic (every
+            # snapshot and commit of this baseline is rounded, the fp64 definition never is)
+            for r in live:
+                s = int(slots[r])
+                ts.H[s] = S[s].float().cpu().numpy().astype(np.float64)
+    un = H.unused_slots(cfg, init)
+    assert torch.equal(S[un], S_init[un]), 'unused slot state modified'
+    print(f'[{cfg.name} snapshot] worst {worst:.2e}', flush=True)
+    return worst
+
+
+@pytest.mark.parametrize('name,cfg', [
+    ('decode_T3', W.CONFIGS['c1'].with_(B=9, null_rows=2, hk=2, hv=4, T=3, accept=('uniform', 0, 3),
+                                        cursor_init='zero')),
+    ('spec_bf16_nan', W.CONFIGS['c2'].with_(B=7, hk=2, hv=4)),
+    ('kda', W.CONFIGS['c3'].with_(B=5, hk=3, hv=3)),
+    ('odd_shapes', W.CONFIGS['c0'].with_(B=3, hk=1, hv=2, dk=48, dv=32, T=2, L=2,
+                                         accept=('uniform', 0, 2))),
+])
+def test_snapshot_baseline(name, cfg):
+    _run_snapshot(cfg, steps=5)
+
+
+def test_snapshot_matches_ring_verify():
+    """The baseline and the ReplaySSM verify of the same workload (full decode shapes at
+    T = 3, one step from cursor 0) give the same outputs within tolerance."""
+    import linear_attention_recurrent_rs_amd as rs
+    cfg = W.CONFIGS['c1'].with_(T=3, accept=('uniform', 1, 3), cursor_init='zero', steps=1)
+    init = H.initial(cfg)
+    g = H.GpuRun(cfg, init)
+    acc, ins, pol, next_T = H.step_data(cfg, 0)
+    ring_out, _ = g.verify(0, g.inputs_dev(ins[0]))
+    snaps = torch.empty((cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv), device='cuda')
+    out = torch.full((cfg.B * cfg.T, cfg.hv, cfg.dv), H.SENTINEL_OUT, device='cuda')
+    S = H.to_dev(init.S[0], cfg.state_dtype, 'cuda')
+    slot_d = torch.from_numpy(init.slots.astype(np.int32)).cuda()
+    rs.snapshot_verify(g.d, False, *_dev_inputs(cfg, ins[0]), S, snaps, slot_d, out)
+    live = torch.from_numpy(np.repeat(init.slots >= 0, cfg.T))
+    a, b = out[live.cuda()].cpu().numpy(), ring_out[live.cuda()].cpu().numpy()
+    assert H.rel_err(a, b) <= 1e-4
