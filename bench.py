@@ -25,7 +25,8 @@ folding); and full step loops (verify per layer, cursor advance, commit folds by
 of the spec-verify (batch 128, bf16 state, T = 4, fold every commit), KDA (batch 64, T = 3)
 and large-ring (batch 256, ring 64, T = 8, 4 layers, forced commit folds) workloads and of
 ragged GDN and KDA verifies (batch 64, widths U{0..4} per row from one packed token list),
-each with verify and commit-fold kernel times and verified / committed tokens per second.
+each with verify and commit-fold kernel times and verified / committed tokens per second;
+and the snapshot-verify baseline on the spec-verify shapes (time and per-layer memory).
 """
 from __future__ import annotations
 
@@ -455,6 +456,65 @@ def run_workload(name, steps=30, warmup=10, tile_v=0):
     return res
 
 
+def snapshot_baseline(name='c2', steps=30, warmup=10):
+    """The snapshot-verify baseline on a workload's shapes (one layer): a verify that writes
+    the state after every draft token, then a commit that copies the accepted snapshot into
+    the state, against ReplaySSM's ring of records.  Kernel times from HIP events; memory =
+    the per-layer buffers each design keeps for the batch."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    cfg = W.CONFIGS[name]
+    st = _rand_setup(cfg, 1)
+    dev, slots_np, d = st['dev'], st['slots_np'], st['d']
+    sd = torch.bfloat16 if cfg.state_dtype == 'bf16' else torch.float32
+    snaps = torch.empty(cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv, dtype=sd, device=dev)
+    out = torch.empty(cfg.B * cfg.T, cfg.hv, cfg.dv, device=dev)
+    sets = [st['inputs']() for _ in range(4)]
+    total = warmup + steps
+    accs = [torch.from_numpy(W.accept_lengths(cfg, j).astype(np.int32)).to(dev)
+            for j in range(total)]
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+    stream = torch.cuda.current_stream()
+    ev_v, ev_c = [], []
+
+    def step(j, timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record(stream)
+        rs.snapshot_verify(d, cfg.kda, *sets[j % 4], st['S'][0], snaps, st['slots'], out,
+                           stream=stream)
+        if timed:
+            e[1].record(stream)
+        rs.snapshot_commit(d, st['S'][0], snaps, st['slots'], accs[j], stream=stream)
+        if timed:
+            e[2].record(stream)
+            ev_v.append((e[0], e[1]))
+            ev_c.append((e[1], e[2]))
+
+    for j in range(warmup):
+        step(j, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(warmup, total):
+        step(j, True)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    acc_sum = float(np.mean([int(accs[j][live].sum()) for j in range(warmup, total)]))
+    s_bytes = 2 if cfg.state_dtype == 'bf16' else 4
+    a_bytes = 2 if cfg.act_dtype == 'bf16' else 4
+    g_ring = cfg.hv * cfg.dk * 4 if cfg.kda else cfg.hv * 4
+    ring = cfg.L * (cfg.hk * cfg.dk * a_bytes + cfg.hv * cfg.dv * 4 + g_ring)
+    return {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'state': cfg.state_dtype,
+            'ms_per_step': round(step_s * 1e3, 5),
+            'verify_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_v])) * 1e3, 3),
+            'commit_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_c])) * 1e3, 3),
+            'verified_tokens_per_s_per_layer': round(len(live) * cfg.T / step_s, 1),
+            'committed_tokens_per_s_per_layer': round(acc_sum / step_s, 1),
+            'snapshot_bytes_per_layer': cfg.B * cfg.T * cfg.hv * cfg.dk * cfg.dv * s_bytes,
+            'ring_bytes_per_layer': cfg.B * ring}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -472,7 +532,7 @@ def main():
                     help='skip the history states and the other workloads')
     ap.add_argument('--only-workload', default='',
                     help='run one of the other workloads (c2, c3, c4, ragged_gdn, '
-                         'ragged_kda) alone and exit')
+                         'ragged_kda, snapshot_c2) alone and exit')
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -485,7 +545,10 @@ def main():
         sys.exit(2)
 
     if args.only_workload:
-        print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
+        if args.only_workload.startswith('snapshot_'):
+            print(json.dumps(snapshot_baseline(args.only_workload[len('snapshot_'):])), flush=True)
+        else:
+            print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -545,6 +608,8 @@ def main():
         for name in ('c2', 'c3', 'c4', 'ragged_gdn', 'ragged_kda'):
             extra[name] = run_workload(name)
             print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
+        extra['snapshot_baseline_c2'] = snapshot_baseline('c2')
+        print(f'# snapshot baseline: {extra["snapshot_baseline_c2"]}', file=sys.stderr, flush=True)
     if extra:
         line['extra'] = extra
     if not args.no_cpu_baseline:
