@@ -147,6 +147,26 @@ __device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, s
 
 // Element p (0..7) of four rows' 8-column chunks (one per row, 4 dwords of bf16 pairs),
 // packed as four bf16 K entries (rows 0..3) of an MFMA operand.
+// Four fp32 values split into three bf16 parts, x = hi + mid + lo + e with
+// |e| <= 2^-24 |x|: hi and mid keep the upper 16 bits of x and of the exact remainder,
+// lo is the final remainder rounded to nearest even.
+__device__ __forceinline__ void split4x3(const float (&x)[4], s4& hi, s4& mid, s4& lo) {
+  uint32_t h[4], m[4];
+  f2 r[2];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w = __float_as_uint(x[e]);
+    h[e] = w & 0xffff0000u;
+    const float r1 = x[e] - __uint_as_float(h[e]);
+    m[e] = __float_as_uint(r1) & 0xffff0000u;
+    r[e >> 1][e & 1] = r1 - __uint_as_float(m[e]);
+  }
+  hi = __builtin_bit_cast(s4, u2{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]});
+  mid = __builtin_bit_cast(s4, u2{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]});
+  lo = __builtin_bit_cast(s4, u2{__builtin_bit_cast(uint32_t, __builtin_convertvector(r[0], b2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(r[1], b2))});
+}
+
 __device__ __forceinline__ s4 column_of(const u4 (&r)[4], int p) {
   const int q = p >> 1, sh = (p & 1) * 16;
   const uint32_t e0 = (r[0][q] >> sh) & 0xffffu, e1 = (r[1][q] >> sh) & 0xffffu;
@@ -190,6 +210,10 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   constexpr int RL = 64 / CC;                            // row groups per wave
   constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && TMAX >= 3;
+  // GDN, fp32 state, 64-column tiles in this lane mapping, windows of 2 and more: the
+  // fused fold on bf16 MFMAs (step 7).  (At window 1 it frees enough registers for six
+  // workgroups per CU, which measured slower than the VALU fold at five.)
+  constexpr bool MFMA_FOLD = !KDA && sizeof(ST) == 4 && CC == 16 && !ADJ && TMAX >= 2;
   const int cc = ADJ ? lane / RL : tid % CC;
   const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
@@ -606,15 +630,63 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[j][i] *= KDA ? Gamv[r0 + i] : Gam;
     }
+    if constexpr (MFMA_FOLD) {
+      // S += K (gamma (.) D)^T over records in blocks of 16 on v_mfma_f32_16x16x16_bf16.
+      // The tile registers are the accumulators: for fixed (j, jj), lane l holds rows
+      // 16 wave + 64 j + 4 (l / 16) + i at column 4 (l % 16) + jj, which is element i of
+      // D[4 (l / 16) + i][l % 16] of a 16 x 16 block.  A = the keys of the block's rows
+      // (bf16, exact), B = gamma_i d_i in three bf16 parts (error <= 2^-24), lane group
+      // l / 16 taking records 4 (l / 16) .. +3 of the block; records past n are selected
+      // to zero, never read into the product.
+      const int lc = lane & 15, lg = lane >> 4;
+      for (int rb = 0; rb < nh; rb += 16) {
+        int recs[4];
+        bool ok[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rec = rb + 4 * lg + e;
+          ok[e] = rec < nh;
+          recs[e] = ok[e] ? rec : 0;
+        }
+        s4 ka[QPT];
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) {
+          const int row = 16 * wave + 64 * j + lc;
+          s4 kv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = ok[e] ? short(hkeys[recs[e] * KS + row]) : short(0);
+          ka[j] = kv;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = ok[e] ? hd[recs[e] * BV + 4 * lc + jj] * gam_i[recs[e]] : 0.f;
+          s4 bh, bm, bl;
+          split4x3(x, bh, bm, bl);
+#pragma unroll
+          for (int j = 0; j < QPT; ++j) {
+            f4 acc = f4{s[j][0][jj], s[j][1][jj], s[j][2][jj], s[j][3][jj]};
+            acc = mfma_bf16_16x16x16(ka[j], bh, acc);
+            acc = mfma_bf16_16x16x16(ka[j], bm, acc);
+            acc = mfma_bf16_16x16x16(ka[j], bl, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[j][i][jj] = acc[i];
+          }
+        }
+      }
+    } else {
 #pragma unroll 4
-    for (int i = 0; i < nh; ++i) {
-      const f4 dq = load4(hd + i * BV + 4 * cc) * (KDA ? 1.f : gam_i[i]);
+      for (int i = 0; i < nh; ++i) {
+        const f4 dq = load4(hd + i * BV + 4 * cc) * (KDA ? 1.f : gam_i[i]);
 #pragma unroll
-      for (int j = 0; j < QPT; ++j) {
-        const int r0 = 4 * (rg + RG * j);
-        const f4 kq = KDA ? load4(khat + i * DK + r0) : bf16x4(hkeys + i * KS + r0);
+        for (int j = 0; j < QPT; ++j) {
+          const int r0 = 4 * (rg + RG * j);
+          const f4 kq = KDA ? load4(khat + i * DK + r0) : bf16x4(hkeys + i * KS + r0);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) s[j][ii] += kq[ii] * dq;
+          for (int ii = 0; ii < 4; ++ii) s[j][ii] += kq[ii] * dq;
+        }
       }
     }
     ST* so = static_cast<ST*>(a.state) + (((size_t)slot * hv + h) * DK) * dv + col0;
