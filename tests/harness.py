@@ -89,7 +89,7 @@ def step_data(cfg: W.Config, j: int):
 
 # ----------------------------------------------------------------------------- GPU side
 
-class GpuRun:
+class DeviceRun:
     def __init__(self, cfg: W.Config, init: Initial, dev='cuda', tile_v: int = 0):
         import linear_attention_recurrent_rs_amd as rs
         self.rs, self.cfg, self.dev = rs, cfg, dev
@@ -236,7 +236,7 @@ class StepReport:
     ints_exact: bool = True
 
 
-def compare_step(cfg: W.Config, g: GpuRun, o: OracleRun, g_outs, g_wps, o_outs, o_wps, acc,
+def compare_step(cfg: W.Config, g: DeviceRun, o: OracleRun, g_outs, g_wps, o_outs, o_wps, acc,
                  rows: List[int], init: Initial, check_state: bool = True) -> StepReport:
     rep = StepReport()
     tol = tol_for(cfg)
@@ -292,7 +292,7 @@ def unused_slots(cfg: W.Config, init: Initial) -> List[int]:
     return [s for s in range(cfg.num_slots) if s not in used]
 
 
-def check_untouched(cfg: W.Config, g: GpuRun, init: Initial):
+def check_untouched(cfg: W.Config, g: DeviceRun, init: Initial):
     """Slots no row maps to keep their state, ring and cursor bit for bit."""
     un = unused_slots(cfg, init)
     if not un:

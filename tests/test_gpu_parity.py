@@ -34,7 +34,7 @@ REDUCED = {
 
 def _run(cfg, rows=None, steps=None, tile_v=0):
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init, tile_v=tile_v)
+    g = H.DeviceRun(cfg, init, tile_v=tile_v)
     o = H.OracleRun(cfg, init, rows=rows)
     rows = list(range(cfg.B)) if rows is None else rows
     worst = H.StepReport()
@@ -71,7 +71,7 @@ def test_c0_against_golden():
     gold = json.load(open(os.path.join(HERE, 'golden', 'c0_oracle.json')))
     # replay the GPU run again, checking each step against the stored fixture
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     for j, st in enumerate(gold['steps']):
         acc, ins, pol, next_T = H.step_data(cfg, j)
         outs, wps = g.step(acc, ins, pol, next_T)
@@ -147,7 +147,7 @@ def test_error_codes():
     import linear_attention_recurrent_rs_amd as rs
     cfg = REDUCED['c1']
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     acc, ins, pol, next_T = H.step_data(cfg, 0)
     q, k, v, beta, gate = g.inputs_dev(ins[0])
     args = [q, k, v, beta, gate, g.S[0], g.rk[0], g.rd[0], g.rg[0], g.cursor, g.slots, g.out,
@@ -173,7 +173,7 @@ def test_empty_batch_and_all_null():
     import linear_attention_recurrent_rs_amd as rs
     cfg = REDUCED['c1'].with_(B=4, null_rows=4, steps=2)
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     for j in range(2):
         acc, ins, pol, next_T = H.step_data(cfg, j)
         outs, wps = g.step(acc, ins, pol, next_T)
@@ -214,9 +214,9 @@ def test_ragged_empty_and_full_windows():
     import linear_attention_recurrent_rs_amd as rs
     cfg = RAGGED['gdn'].with_(steps=3)
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     o = H.OracleRun(cfg, init)
-    u = H.GpuRun(cfg, init)                      # the same workload through the uniform call
+    u = H.DeviceRun(cfg, init)                      # the same workload through the uniform call
     zeros = np.zeros(cfg.B, np.int32)
     acc, ins, pol, next_T = H.step_data(cfg, 0)
     S0 = [x.clone() for x in g.S]

@@ -38,7 +38,7 @@ LARGE = W.CONFIGS['c4'].with_(B=5, hk=2, hv=4, steps=20)
 @pytest.mark.parametrize('cfg', [SPEC, KDA, LARGE], ids=['spec_bf16', 'kda', 'large_ring'])
 def test_deterministic(cfg):
     init = H.initial(cfg)
-    a, b = H.GpuRun(cfg, init), H.GpuRun(cfg, init)
+    a, b = H.DeviceRun(cfg, init), H.DeviceRun(cfg, init)
     for j in range(cfg.steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
         oa, wa = a.step(acc, ins, pol, next_T)
@@ -53,7 +53,7 @@ def test_deterministic(cfg):
 def test_nan_isolation_bitwise():
     cfg = SPEC.with_(nan_frac=0.5)           # many poisoned rejected positions
     init = H.initial(cfg)
-    poisoned, clean = H.GpuRun(cfg, init), H.GpuRun(cfg, init)
+    poisoned, clean = H.DeviceRun(cfg, init), H.DeviceRun(cfg, init)
     n_injected = 0
     for j in range(cfg.steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
@@ -85,8 +85,8 @@ def test_commit_fold_equals_history_replay():
     base = W.CONFIGS['c1'].with_(B=9, null_rows=1, hk=2, hv=4, T=3, accept=('uniform', 0, 3),
                                  steps=14, cursor_init='zero')
     init = H.initial(base)
-    keep = H.GpuRun(base, init)
-    fold = H.GpuRun(base.with_(policy='every_commit'), init)
+    keep = H.DeviceRun(base, init)
+    fold = H.DeviceRun(base.with_(policy='every_commit'), init)
     worst = 0.0
     for j in range(base.steps):
         acc, ins, _, _ = H.step_data(base, j)
@@ -113,7 +113,7 @@ def test_graph_replay_matches_eager():
     cfg = W.CONFIGS['c1'].with_(B=12, null_rows=2, hk=2, hv=4, T=3, accept=('uniform', 1, 3),
                                 layers=2, steps=6)
     init = H.initial(cfg)
-    eager, graphed = H.GpuRun(cfg, init), H.GpuRun(cfg, init)
+    eager, graphed = H.DeviceRun(cfg, init), H.DeviceRun(cfg, init)
     BT = cfg.B * cfg.T
     dev = 'cuda'
     static = [tuple(torch.zeros_like(x) for x in graphed.inputs_dev(H.step_data(cfg, 0)[1][l]))
@@ -159,7 +159,7 @@ def test_graph_replay_matches_eager():
 
 def _sampled(cfg, rows, steps):
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     o = H.OracleRun(cfg, init, rows=rows)
     worst = H.StepReport()
     for j in range(steps):

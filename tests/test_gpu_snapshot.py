@@ -108,7 +108,7 @@ def test_snapshot_matches_ring_verify():
     import linear_attention_recurrent_rs_amd as rs
     cfg = W.CONFIGS['c1'].with_(T=3, accept=('uniform', 1, 3), cursor_init='zero', steps=1)
     init = H.initial(cfg)
-    g = H.GpuRun(cfg, init)
+    g = H.DeviceRun(cfg, init)
     acc, ins, pol, next_T = H.step_data(cfg, 0)
     ring_out, _ = g.verify(0, g.inputs_dev(ins[0]))
     snaps = torch.empty((cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv), device='cuda')
