@@ -183,6 +183,13 @@ __host__ __device__ constexpr bool fast_f32_split(bool kda, bool bf16_state, int
   return !kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4 || tmax == 8);
 }
 
+// The same for KDA (fp32 state, 64-column tiles, window 4): the decayed readout vectors
+// split into high and mid bf16 parts (kept where the fp32 vectors would be), the state into
+// high and low parts, three MFMAs per block.  (At window 3 the FMA readout measured faster.)
+__host__ __device__ constexpr bool fast_kda_split(bool kda, bool bf16_state, int bv, int tmax) {
+  return kda && !bf16_state && bv == 64 && tmax == 4;
+}
+
 inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T, int L) {
   auto al = [](int x) { return (x + 15) & ~15; };
   const int dk = 128, vpp = readout_vpp(tmax), ks = kKeyStride;
@@ -193,7 +200,8 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
   l.cs = (2 * tmax + 15) & ~15;
   l.lp = (L + 15) & ~15;
   const bool bfm = fast_bf16_mfma(kda, bf16_state, bv, tmax);
-  const bool all_vec = (bv == 64 && tmax >= 8) || bfm || fast_f32_split(kda, bf16_state, bv, tmax);
+  const bool all_vec = (bv == 64 && tmax >= 8) || bfm || fast_f32_split(kda, bf16_state, bv, tmax) ||
+                       fast_kda_split(kda, bf16_state, bv, tmax);
   const int red_bytes = al(4 * (all_vec ? l.nvec_pad : vpp) * bv * 4);
   l.xkq = o; o += al(2 * tmax * ks * 2);
   l.xv = o; o += al(tmax * bv * 2);

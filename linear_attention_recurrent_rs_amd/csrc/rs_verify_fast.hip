@@ -199,6 +199,9 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   // GDN with an fp32 state, 64-column tiles, windows 3-4: the same MFMA readout over the
   // state split into high and low bf16 parts (two MFMAs per block; step 8)
   constexpr bool F32_SPLIT = fast_f32_split(KDA, sizeof(ST) == 2, BV, TMAX);
+  // KDA with an fp32 state, 64-column tiles, window 4: readout on bf16 MFMAs with both
+  // operands split (step 8)
+  constexpr bool KDA_SPLIT = fast_kda_split(KDA, sizeof(ST) == 2, BV, TMAX);
   constexpr int NTILE = BF16_MFMA ? 8 : QPT * 4;          // tile load instructions
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Lane mapping.  Column quad fastest (cc = lane % CC) makes 16 consecutive lanes read
@@ -209,7 +212,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   // row segments).
   constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   constexpr int RL = 64 / CC;                            // row groups per wave
-  constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && TMAX >= 3;
+  constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && !KDA_SPLIT && TMAX >= 3;
   // GDN, fp32 state, 64-column tiles in this lane mapping, windows of 2 and more: the
   // fused fold on bf16 MFMAs (step 7).  (At window 1 it frees enough registers for six
   // workgroups per CU, which measured slower than the VALU fold at five.)
@@ -411,11 +414,24 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
       Gamv[tid] = g;
       const float scale = fold ? 1.f : g;
-      for (int t = 0; t < T; ++t) {
-        xr[(2 * t) * XS + tid] = scale * xs[t * XS + tid];
-        xr[(2 * t + 1) * XS + tid] = scale * xs[(T + t) * XS + tid];
+      if constexpr (KDA_SPLIT) {
+        // readout vectors in xs order (q_0.., then k_0..) as bf16 parts, x = hi + mid + e
+        // with |e| <= 2^-17 |x|: hi rows [0, 2T), mid rows [nvec_pad, nvec_pad + 2T), XS
+        // elements apart, in the space of the fp32 vectors
+        bf16* xb = reinterpret_cast<bf16*>(xr);
+        for (int v = 0; v < 2 * T; ++v) {
+          const float x = scale * xs[v * XS + tid];
+          const uint32_t w = __float_as_uint(x);
+          xb[v * XS + tid] = bf16(w >> 16);
+          xb[(lay.nvec_pad + v) * XS + tid] = bf16_rne(x - __uint_as_float(w & 0xffff0000u));
+        }
+      } else {
+        for (int t = 0; t < T; ++t) {
+          xr[(2 * t) * XS + tid] = scale * xs[t * XS + tid];
+          xr[(2 * t + 1) * XS + tid] = scale * xs[(T + t) * XS + tid];
+        }
+        for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
       }
-      for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
     }
     lds_barrier();
   }
@@ -527,7 +543,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
   //   the history part, step 8.)
   const int NP = lay.nvec_pad;
-  if ((MFMA_READOUT || BF16_MFMA || F32_SPLIT) && hrows > 0) {
+  if ((MFMA_READOUT || BF16_MFMA || F32_SPLIT || KDA_SPLIT) && hrows > 0) {
     constexpr int NCB = BV / 16, NVB = (NV2 + 15) / 16;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -803,6 +819,54 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
           float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
                     (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
           p *= scale * Gp[m >> 1];
+          if (hrows > 0) p += hist[m * BV + tid];
+          Pv[m] = p;
+        }
+      }
+    }
+  } else if constexpr (KDA_SPLIT) {
+    // R_v = S^T x_v, x_v the decayed vectors (xs order) = hi + mid, S = hi + lo: three
+    // bf16 MFMAs per block (hi.hi, hi.lo, mid.hi), lane layout as in the split readout
+    // above; the decays are inside x, so P = R + the history part.
+    const int lc = lane & 15, lg = lane >> 4;
+    const bf16* xb = reinterpret_cast<const bf16*>(xr);
+    const int NPd = lay.nvec_pad;
+    f4 D[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) D[p] = f4{0.f, 0.f, 0.f, 0.f};
+    const s4 zero4 = s4{0, 0, 0, 0};
+    const bool vok = lc < nvec;
+    const int vrow = vok ? lc : 0;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int r = 4 * (rg + RG * j);
+      const s4 xh = *reinterpret_cast<const s4*>(xb + vrow * XS + r);
+      const s4 xm = *reinterpret_cast<const s4*>(xb + (NPd + vrow) * XS + r);
+      const s4 ah = vok ? xh : zero4, am = vok ? xm : zero4;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        s4 bh, bl;
+        split4(s[j][0][p], s[j][1][p], s[j][2][p], s[j][3][p], bh, bl);
+        D[p] = mfma_bf16_16x16x16(ah, bh, D[p]);
+        D[p] = mfma_bf16_16x16x16(ah, bl, D[p]);
+        D[p] = mfma_bf16_16x16x16(am, bh, D[p]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 4 * lg + e;
+      if (v < nvec) {
+        const int m = v < T ? 2 * v : 2 * (v - T) + 1;
+        store4(red + (wave * NPd + m) * BV + 4 * lc, f4{D[0][e], D[1][e], D[2][e], D[3][e]});
+      }
+    }
+    lds_barrier();
+    if (tid < BV) {
+#pragma unroll
+      for (int m = 0; m < NV2; ++m) {
+        if (m < nvec) {
+          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
+                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
           if (hrows > 0) p += hist[m * BV + tid];
           Pv[m] = p;
         }
