@@ -111,3 +111,21 @@ def test_varlen_validation():
                None) == 4
     empty = _dims(batch=0)
     assert lib.rs_gdn_verify_varlen(ctypes.byref(empty), None, 0, *([None] * 14), None) == 0
+
+
+def test_snapshot_validation():
+    """The snapshot-verify baseline validates like the ring calls: RS_E_SHAPE for bad dims
+    or KDA with hv != hk, RS_E_RING_TOO_SMALL when the ring cannot hold T, RS_E_NULLPTR for
+    missing buffers, and an empty batch is a no-op."""
+    lib = rs._lib()
+    d = _dims(T=4)
+    assert lib.rs_snapshot_verify(ctypes.byref(d), 0, *([None] * 9), None) == 1
+    assert lib.rs_snapshot_verify(ctypes.byref(d), 1, *([None] * 9), None) == 2   # hv != hk
+    assert lib.rs_snapshot_verify(ctypes.byref(_dims(T=0)), 0, *([None] * 9), None) == 2
+    assert lib.rs_snapshot_verify(ctypes.byref(_dims(T=4, ring_cap=3)), 0, *([None] * 9),
+                                  None) == 4
+    assert lib.rs_snapshot_commit(ctypes.byref(d), *([None] * 4), None) == 1
+    assert lib.rs_snapshot_commit(ctypes.byref(_dims(T=17)), *([None] * 4), None) == 2
+    empty = _dims(batch=0, T=4)
+    assert lib.rs_snapshot_verify(ctypes.byref(empty), 0, *([None] * 9), None) == 0
+    assert lib.rs_snapshot_commit(ctypes.byref(empty), *([None] * 4), None) == 0
