@@ -7,7 +7,7 @@
 * fold invariance on the GPU: committing (folding) after every step and never folding
   give the same accepted outputs and the same materialized state, within tolerance;
 * HIP graph replay: a captured decode step, replayed with fresh inputs copied in between,
-  matches the eager launches bit for bit, replay after replay;
+  matches the eager launches bit for bit, replay after replay (uniform and ragged windows);
 * full-size workloads: every row and head on the GPU, sampled rows checked against the
   oracle, at the sizes and in the launch configuration the benchmark uses.
 """
@@ -207,3 +207,65 @@ def test_full_size_ragged_sampled():
     U{0..4}, staggered cursors)."""
     cfg = W.CONFIGS['ragged_gdn'].with_(steps=8)
     _sampled(cfg, _rows(cfg, 4), cfg.steps)
+
+
+def test_graph_replay_ragged_matches_eager():
+    """Ragged windows under graph capture: the cumulative lengths and the packed tokens sit
+    in fixed-capacity device buffers captured once (capacity B * T tokens); between
+    replays only their contents change, so each step may pack a different set of widths.
+    Every replay matches eager ragged launches bit for bit."""
+    import linear_attention_recurrent_rs_amd as rs
+    cfg = W.CONFIGS['ragged_gdn'].with_(B=10, null_rows=2, hk=2, hv=4, layers=2, steps=6)
+    init = H.initial(cfg)
+    eager, graphed = H.DeviceRun(cfg, init), H.DeviceRun(cfg, init)
+    cap = cfg.B * cfg.T
+    dev = 'cuda'
+    gsh = (cfg.hv, cfg.dk) if cfg.kda else (cfg.hv,)
+    at = H.torch_dtype(cfg.act_dtype)
+    static = [(torch.zeros(cap, cfg.hk, cfg.dk, dtype=at, device=dev),
+               torch.zeros(cap, cfg.hk, cfg.dk, dtype=at, device=dev),
+               torch.zeros(cap, cfg.hv, cfg.dv, dtype=at, device=dev),
+               torch.zeros(cap, cfg.hv, dtype=at, device=dev),
+               torch.zeros((cap,) + gsh, dtype=at, device=dev)) for _ in range(cfg.layers)]
+    cu_buf = torch.zeros(cfg.B + 1, dtype=torch.int32, device=dev)
+    acc_buf = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+    outs = [torch.full((cap, cfg.hv, cfg.dv), H.SENTINEL_OUT, device=dev) for _ in range(cfg.layers)]
+    calls = [rs.prepare_verify_varlen(False, graphed.d, cu_buf, *static[l], graphed.S[l],
+                                      graphed.rk[l], graphed.rd[l], graphed.rg[l],
+                                      graphed.cursor, graphed.slots, outs[l], graphed.wp,
+                                      graphed.counter) for l in range(cfg.layers)]
+    adv = rs.prepare_cursor_advance_varlen(graphed.d, cu_buf, cap, graphed.cursor,
+                                           graphed.fold_len, graphed.slots, acc_buf,
+                                           rs.FOLD_NONE, cfg.T)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            s = torch.cuda.current_stream()
+            for l in range(cfg.layers):
+                calls[l](s)
+            adv(s)
+    torch.cuda.synchronize()
+    for j in range(cfg.steps):
+        acc, ins, pol, next_T = H.step_data(cfg, j)
+        lens = H.step_windows(cfg, j)
+        cu, idx, _ = H.pack_windows(lens, cfg.T)
+        graphed.set_windows(lens)
+        for l in range(cfg.layers):
+            for dst, src in zip(static[l], graphed.inputs_dev(ins[l])):
+                dst.zero_()
+                dst[:src.shape[0]].copy_(src)
+            outs[l].fill_(H.SENTINEL_OUT)
+        cu_buf.copy_(torch.from_numpy(cu))
+        acc_buf.copy_(torch.from_numpy(acc.astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eo, _ = eager.step(acc, ins, pol, next_T, lens=lens)
+        torch.cuda.synchronize()
+        sel = torch.from_numpy(idx).to(dev)
+        for l in range(cfg.layers):
+            assert _same(outs[l][:len(idx)], eo[l][sel]), f'replay {j} layer {l}: outputs differ'
+            assert _same(graphed.S[l], eager.S[l]) and _same(graphed.rd[l], eager.rd[l])
+        assert torch.equal(graphed.cursor, eager.cursor), f'replay {j}: cursors differ'
