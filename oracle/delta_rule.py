@@ -15,7 +15,8 @@ S = S_math^T the same rule is
     S'  = alpha (.) S          GDN: scalar alpha; KDA: row i (key channel i) times alpha[i]
     d   = beta (v - S'^T k)    the fp32 "delta" / update the history ring stores
     S   = S' + k d^T
-    o   = S^T q                (read from the post-update state, scale 1)
+    o   = scale S^T q          (read from the post-update state; scale is the caller's
+                                query scale, applied to the output and nothing else)
 
 Expanding (I - beta k k^T) shows the two forms are equal; ``oracle.exact`` evaluates the
 dense left-hand form in rational arithmetic and the pin tests hold this one to it.
@@ -51,9 +52,9 @@ def token_update(S, k, v, beta, alpha, kda: bool):
     return Sd + np.einsum('...i,...j->...ij', k, d), d
 
 
-def readout(S, q):
-    """o = S^T q over the key axis: S [..., dk, dv], q [..., dk] -> [..., dv]."""
-    return np.einsum('...ij,...i->...j', S, q)
+def readout(S, q, scale=1.0):
+    """o = scale * S^T q over the key axis: S [..., dk, dv], q [..., dk] -> [..., dv]."""
+    return float(scale) * np.einsum('...ij,...i->...j', S, q)
 
 
 def apply_record(S, k, d, alpha, kda: bool):
@@ -71,13 +72,13 @@ def fold(S, ks, ds, gs, kda: bool):
     return S
 
 
-def run_tokens(S, ks, vs, betas, alphas, qs, kda: bool):
+def run_tokens(S, ks, vs, betas, alphas, qs, kda: bool, scale=1.0):
     """Sequential recurrence over tokens t = 0..T-1 (leading axis).  Returns
     (final state, outputs [T, ..., dv], deltas [T, ..., dv], states after each token)."""
     outs, dels, states = [], [], []
     for t in range(len(ks)):
         S, d = token_update(S, ks[t], vs[t], betas[t], alphas[t], kda)
-        outs.append(readout(S, qs[t]))
+        outs.append(readout(S, qs[t], scale))
         dels.append(d)
         states.append(S)
     return S, np.array(outs), np.array(dels), states

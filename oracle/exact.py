@@ -3,7 +3,7 @@
 Evaluates, with ``fractions.Fraction``, the key-to-value orientation exactly as the rule
 is usually written:
 
-    S_t = S_{t-1} . A_t . (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = S_t q_t,
+    S_t = S_{t-1} . A_t . (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = scale S_t q_t,
 
 S_t of shape [dv, dk], A_t = alpha_t I (GDN) or diag(alpha_t) (KDA).  It forms the dense
 dk x dk matrix (I - beta k k^T) and multiplies full matrices, so it shares no
@@ -60,15 +60,16 @@ def dense_step(S: Matrix, k, v, beta, alpha, kda: bool) -> Matrix:
     return _add(_matmul(_matmul(S, A), P), _scale(_outer(v, k), Fraction(beta)))
 
 
-def dense_output(S: Matrix, q) -> List[Fraction]:
-    return [sum((S[i][j] * q[j] for j in range(len(q))), Fraction(0)) for i in range(len(S))]
+def dense_output(S: Matrix, q, scale=Fraction(1)) -> List[Fraction]:
+    return [Fraction(scale) * sum((S[i][j] * q[j] for j in range(len(q))), Fraction(0))
+            for i in range(len(S))]
 
 
-def run(S0: Matrix, tokens, kda: bool):
+def run(S0: Matrix, tokens, kda: bool, scale=Fraction(1)):
     """tokens: list of (q, k, v, beta, alpha) with Fraction entries.  Returns (final S,
-    outputs per token)."""
+    outputs per token, each scaled by the query scale)."""
     S, outs = S0, []
     for (q, k, v, beta, alpha) in tokens:
         S = dense_step(S, k, v, beta, alpha, kda)
-        outs.append(dense_output(S, q))
+        outs.append(dense_output(S, q, scale))
     return S, outs

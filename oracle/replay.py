@@ -59,6 +59,25 @@ def lazy_fold(m: int, next_T: int, L: int) -> bool:
     return m + next_T > L
 
 
+def policy_folds(policy: int, m: int, next_T: int, L: int, masked_in: bool) -> bool:
+    """Whether the commit folds a row that ends its step with m committed records.
+
+    EVERY_COMMIT folds every accepted window into S (sglang commit 4: the DFLASH/DSPARK
+    commit folds the accepted window into the checkpoint).  LAZY folds only when the next
+    verify, of width next_T, would not fit in the ring (LightLLM lazy compaction; sglang
+    commit 4: the lazy fold's early flush reads the draft length).  FORCE folds the rows
+    the caller selects (LightLLM force_compress).  NONE leaves every fold to the verify."""
+    if policy == FOLD_NONE:
+        return False
+    if policy == FOLD_EVERY_COMMIT:
+        return True
+    if policy == FOLD_LAZY:
+        return lazy_fold(m, next_T, L)
+    if policy == FOLD_FORCE:
+        return bool(masked_in)
+    raise ValueError(policy)
+
+
 def window(T: int, lens, r: int) -> int:
     """Window width of row r: the batch's T, or lens[r] when windows are ragged."""
     return T if lens is None else int(lens[r])
@@ -78,8 +97,8 @@ class ReplayLayer:
     """
 
     def __init__(self, S0, ring_k, ring_d, ring_g, kda: bool, G: int, L: int,
-                 slots: Optional[Iterable[int]] = None):
-        self.kda, self.G, self.L = kda, G, L
+                 slots: Optional[Iterable[int]] = None, scale: float = 1.0):
+        self.kda, self.G, self.L, self.scale = kda, G, L, float(scale)
         idx = range(S0.shape[0]) if slots is None else sorted(set(int(s) for s in slots if s >= 0))
         self.S: Dict[int, np.ndarray] = {s: np.array(S0[s], dtype=np.float64) for s in idx}
         self.rk = {s: np.array(ring_k[s], dtype=np.float64) for s in idx}
@@ -123,7 +142,7 @@ def verify(layer: ReplayLayer, cursor, slots, inp, rows=None, lens=None):
         qs = expand_heads(inp.q[r], G)
         for t in range(T):
             H, d = token_update(H, ks[t], inp.v[r, t], inp.beta[r, t], inp.gate[r, t], kda)
-            out[r, t] = readout(H, qs[t])
+            out[r, t] = readout(H, qs[t], layer.scale)
             layer.rk[s][base + t] = inp.k[r, t]
             layer.rd[s][base + t] = d
             layer.rg[s][base + t] = inp.gate[r, t]
@@ -146,16 +165,8 @@ def cursor_advance(cursor, fold_len, slots, accept, T: int, L: int, policy: int,
         n = int(cursor[s])
         base = 0 if fold_now(n, window(T, lens, r), L) else n
         m = base + int(accept[r])
-        if policy == FOLD_NONE:
-            fl = 0
-        elif policy == FOLD_EVERY_COMMIT:
-            fl = m
-        elif policy == FOLD_LAZY:
-            fl = m if lazy_fold(m, next_T, L) else 0
-        elif policy == FOLD_FORCE:
-            fl = m if (force_mask is None or force_mask[r]) else 0
-        else:
-            raise ValueError(policy)
+        masked_in = force_mask is None or bool(force_mask[r])
+        fl = m if policy_folds(policy, m, next_T, L, masked_in) else 0
         fold_len[s] = fl
         cursor[s] = 0 if fl else m
 
@@ -188,15 +199,15 @@ class TokenStream:
     """The definition: per slot, the committed state is the gated delta rule run over the
     accepted tokens in order; a verify runs the T draft tokens on from it."""
 
-    def __init__(self, committed: Dict[int, np.ndarray], kda: bool, G: int):
+    def __init__(self, committed: Dict[int, np.ndarray], kda: bool, G: int, scale: float = 1.0):
         self.H = {s: np.array(v, dtype=np.float64) for s, v in committed.items()}
-        self.kda, self.G = kda, G
+        self.kda, self.G, self.scale = kda, G, float(scale)
         self._window = {}
 
     @classmethod
     def from_replay(cls, layer: ReplayLayer, cursor):
         return cls({s: layer.committed_state(s, int(cursor[s])) for s in layer.S},
-                   layer.kda, layer.G)
+                   layer.kda, layer.G, layer.scale)
 
     def verify(self, slots, inp, rows=None, lens=None):
         B, Tb = inp.v.shape[:2]
@@ -214,7 +225,7 @@ class TokenStream:
             for t in range(window(Tb, lens, r)):
                 H, d = token_update(H, ks[t], inp.v[r, t], inp.beta[r, t], inp.gate[r, t],
                                     self.kda)
-                out[r, t] = readout(H, qs[t])
+                out[r, t] = readout(H, qs[t], self.scale)
                 dels[r, t] = d
                 states.append(H)
             self._window[s] = states

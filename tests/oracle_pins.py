@@ -465,7 +465,116 @@ def pin_ragged_cursor_bruteforce():
             assert _rel(rp.materialize(layer, cursor, slots)[0], ts.H[0]) < 1e-12
 
 
+def pin_query_scale():
+    """The query scale multiplies the outputs and nothing else: against the exact rational
+    dense rule with scale 3/8 (outputs and the final state), and through the replay state
+    machine, where a layer read out at scale 3/8 gives 3/8 of the scale-1 outputs with
+    bit-identical states, rings and cursors."""
+    rng = np.random.default_rng(24)
+    sc = Fraction(3, 8)
+    for kda in (False, True):
+        dk, dv, T = 3, 2, 4
+        S0 = [_frac_vec(rng, dk) for _ in range(dv)]
+        toks = _tiny_tokens(rng, T, dk, dv, kda)
+        S_ex, outs_ex = exact.run(S0, toks, kda, sc)
+        S = np.array([[float(x) for x in row] for row in S0]).T
+        for t, (q, k, v, beta, alpha) in enumerate(toks):
+            S, _ = dr.token_update(S, _f(k), _f(v), _f(beta), _f(alpha), kda)
+            assert _rel(dr.readout(S, _f(q), float(sc)), _f(outs_ex[t])) < 1e-13, ('scaled', kda, t)
+        S_ex_stored = np.array([[float(x) for x in row] for row in S_ex]).T
+        assert _rel(S, S_ex_stored) < 1e-13, ('scale reached the state', kda)
+    hk, hv, dk, dv, B, T, L, steps = 1, 2, 4, 3, 3, 2, 5, 6
+    S0 = rng.standard_normal((B, hv, dk, dv))
+    slots = np.arange(B, dtype=np.int32)
+    ins = [_inputs(B, T, hk, hv, dk, dv, False, rng) for _ in range(steps)]
+    accs = [rng.integers(0, T + 1, size=B).astype(np.int32) for _ in range(steps)]
+    runs = []
+    for scale in (1.0, float(sc)):
+        layer = _layer(S0, L, hk, hv, dk, dv, False)
+        layer.scale = scale
+        cursor = np.zeros(B, np.int32)
+        fl = np.zeros(B, np.int32)
+        outs = []
+        for j in range(steps):
+            o, _ = rp.verify(layer, cursor, slots, ins[j])
+            outs.append(o)
+            rp.cursor_advance(cursor, fl, slots, accs[j], T, L, rp.FOLD_NONE)
+        runs.append((np.array(outs), layer, cursor.copy()))
+    (o1, l1, c1), (o2, l2, c2) = runs
+    assert _rel(o2, float(sc) * o1) < 1e-15, 'scaled outputs'
+    assert np.array_equal(c1, c2)
+    for s in range(B):
+        assert np.array_equal(l1.S[s], l2.S[s]) and np.array_equal(l1.rd[s], l2.rd[s],
+                                                                   equal_nan=True)
+
+
+def pin_fold_policies():
+    """The commit's fold policies, derived from what a fold means rather than read back
+    from the oracle.  A row's committed records are either in S or in the ring, so after
+    a commit that folds, the canonical S itself equals the definition's committed state
+    and the cursor is 0; after one that does not, S keeps its bits and the cursor counts
+    the records committed since the last fold.  Per policy:
+      EVERY_COMMIT -- every live row ends every step folded;
+      FORCE (seeded per-row masks) -- exactly the masked-in rows fold, the others keep
+        cursor = write_pos + accept and an unchanged S;
+      LAZY (next window widths 1..T+1, not only T) -- a row folds exactly when its m
+        committed records plus the next window would overflow the ring.
+    The pending-record count is kept here by the pin itself: a verify whose window would
+    overflow first folds the whole prefix (then writes at 0), and the accept adds to it."""
+    rng = np.random.default_rng(25)
+    hk, hv, dk, dv, B, T, L, steps = 1, 2, 3, 3, 5, 3, 6, 14
+    nslots = B + 2
+    slots = np.array([4, 0, -1, 6, 2], np.int32)
+    ins = [_inputs(B, T, hk, hv, dk, dv, False, rng) for _ in range(steps)]
+    accs = [rng.integers(0, T + 1, size=B).astype(np.int32) for _ in range(steps)]
+    masks = [rng.integers(0, 2, size=B).astype(np.uint8) for _ in range(steps)]
+    next_Ts = [int(rng.integers(1, T + 2)) for _ in range(steps)]
+    S0 = rng.standard_normal((nslots, hv, dk, dv)) * 0.5
+    for pol in (rp.FOLD_EVERY_COMMIT, rp.FOLD_FORCE, rp.FOLD_LAZY):
+        layer = _layer(S0, L, hk, hv, dk, dv, False)
+        ts = rp.TokenStream.from_replay(layer, np.zeros(nslots, np.int32))
+        cursor = np.zeros(nslots, np.int32)
+        fl = np.zeros(nslots, np.int32)
+        pend = {int(s): 0 for s in slots if s >= 0}
+        folds = stays = 0
+        for j in range(steps):
+            rp.verify(layer, cursor, slots, ins[j])
+            ts.verify(slots, ins[j])
+            base = {}
+            for s in pend:
+                base[s] = 0 if pend[s] + T > L else pend[s]
+            S_before = {s: layer.S[s].copy() for s in pend}
+            rp.cursor_advance(cursor, fl, slots, accs[j], T, L, pol, next_Ts[j], masks[j])
+            rp.commit_fold(layer, fl, slots)
+            ts.accept(slots, accs[j])
+            for r in range(B):
+                s = int(slots[r])
+                if s < 0:
+                    continue
+                m = base[s] + int(accs[j][r])
+                if pol == rp.FOLD_EVERY_COMMIT:
+                    want = True
+                elif pol == rp.FOLD_FORCE:
+                    want = bool(masks[j][r])
+                else:
+                    want = m + next_Ts[j] > L
+                if want:
+                    assert cursor[s] == 0, ('policy must fold', pol, j, r)
+                    assert _rel(layer.S[s], ts.H[s]) < 1e-12, ('folded S is not committed', pol, j)
+                    assert fl[s] == m
+                    pend[s] = 0
+                    folds += m > 0
+                else:
+                    assert cursor[s] == m, ('policy must not fold', pol, j, r, cursor[s], m)
+                    assert np.array_equal(layer.S[s], S_before[s]), ('S changed', pol, j, r)
+                    assert fl[s] == 0
+                    pend[s] = m
+                    stays += 1
+        assert folds > 0 and (pol == rp.FOLD_EVERY_COMMIT or stays > 0), (pol, folds, stays)
+
+
 ALL_PINS = [pin_exact_rational, pin_exact_grouped_heads, pin_pure_decay, pin_identity_readout,
             pin_write_then_read, pin_grouped_write, pin_replay_equals_sequential,
             pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation,
-            pin_ragged_replay_equals_sequential, pin_ragged_cursor_bruteforce]
+            pin_ragged_replay_equals_sequential, pin_ragged_cursor_bruteforce, pin_query_scale,
+            pin_fold_policies]

@@ -47,8 +47,8 @@ def _tu_kda_columns(S, k, v, beta, alpha, kda):
     return Sd + np.einsum('...i,...j->...ij', k, d), d
 
 
-def _readout_transposed(S, q):
-    return np.einsum('...ij,...j->...i', S, q)
+def _readout_transposed(S, q, scale=1.0):
+    return float(scale) * np.einsum('...ij,...j->...i', S, q)
 
 
 def _expand_tile(x, G):
@@ -71,6 +71,35 @@ def _window_ignored(T, lens, r):
     return T
 
 
+def _readout_unscaled(S, q, scale=1.0):
+    return np.einsum('...ij,...i->...j', S, q)
+
+
+def _readout_scaled_twice(S, q, scale=1.0):
+    return float(scale) ** 2 * np.einsum('...ij,...i->...j', S, q)
+
+
+_policy_folds = rp.policy_folds
+
+
+def _every_commit_never(policy, m, next_T, L, masked_in):
+    return False if policy == rp.FOLD_EVERY_COMMIT else _policy_folds(policy, m, next_T, L, masked_in)
+
+
+def _force_ignores_mask(policy, m, next_T, L, masked_in):
+    return True if policy == rp.FOLD_FORCE else _policy_folds(policy, m, next_T, L, masked_in)
+
+
+def _force_mask_inverted(policy, m, next_T, L, masked_in):
+    return (not masked_in) if policy == rp.FOLD_FORCE else _policy_folds(policy, m, next_T, L,
+                                                                          masked_in)
+
+
+def _lazy_ignores_next_width(policy, m, next_T, L, masked_in):
+    return rp.lazy_fold(m, 1, L) if policy == rp.FOLD_LAZY else _policy_folds(policy, m, next_T,
+                                                                                L, masked_in)
+
+
 MUTANTS = {
     'ragged window width ignored': [('window', _window_ignored)],
     'd sign flipped': [('token_update', _tu_sign)],
@@ -83,6 +112,12 @@ MUTANTS = {
     'record replay drops decay': [('apply_record', _apply_record_nodecay)],
     'fused fold one record early': [('fold_now', _fold_now_early)],
     'lazy fold one record late': [('lazy_fold', _lazy_late)],
+    'query scale dropped': [('readout', _readout_unscaled)],
+    'query scale applied twice': [('readout', _readout_scaled_twice)],
+    'every-commit policy never folds': [('policy_folds', _every_commit_never)],
+    'force policy ignores its mask': [('policy_folds', _force_ignores_mask)],
+    'force policy mask inverted': [('policy_folds', _force_mask_inverted)],
+    'lazy policy ignores the next window width': [('policy_folds', _lazy_ignores_next_width)],
 }
 
 
