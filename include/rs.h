@@ -18,7 +18,7 @@
  * state stored as S[dk][dv] per value head:
  *     S' = alpha (.) S        (GDN: scalar alpha; KDA: key row i scaled by alpha[i])
  *     d  = beta * (v - S'^T k)            the "delta", kept in fp32 history
- *     S  = S' + k d^T,        o = S^T q  (post-update state, no extra scale)
+ *     S  = S' + k d^T,        o = scale S^T q  (post-update state; dims->scale)
  * Value head h reads key head h / (hv / hk).
  *
  * ReplaySSM: the canonical state S of a slot stays in place.  A verify of T draft tokens
@@ -60,7 +60,8 @@ typedef enum {
     RS_E_SHAPE = 2,           /* unsupported or inconsistent dimensions */
     RS_E_DTYPE = 3,           /* unsupported dtype */
     RS_E_RING_TOO_SMALL = 4,  /* ring_cap < T: the ring cannot hold the draft window */
-    RS_E_LAUNCH = 5           /* the kernel launch failed (hipGetLastError) */
+    RS_E_LAUNCH = 5,          /* the kernel launch failed (hipGetLastError) */
+    RS_E_VALUE = 6            /* a scalar argument is out of range (dims->scale) */
 } rs_status;
 
 typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
@@ -76,11 +77,15 @@ typedef enum {
 /* Shapes.  batch B: request rows; T: verify window, 1..16; hk, hv: key and value heads
  * (hv % hk == 0; KDA needs hv == hk); dk in {16,32,...,256} and dv a multiple of 16;
  * ring_cap L >= T, L <= 256; num_slots: size of the slot pools; act_dtype: q, k, v, beta,
- * gate and ring keys; state_dtype: S.  tile_v: value columns per workgroup (16, 32, 64 or
- * 128, dividing dv), or 0 for the library's choice. */
+ * gate and ring keys; state_dtype: S.  scale: the query scale, o = scale S^T q (1.0 for
+ * none, dk^-1/2 for the usual attention scale); read by the verifies only, which return
+ * RS_E_VALUE unless it is finite and nonzero (a zero-initialised struct is refused rather
+ * than silently producing zero outputs).  tile_v: value columns per workgroup (16, 32, 64
+ * or 128, dividing dv), or 0 for the library's choice. */
 typedef struct {
     int32_t batch, T, hk, hv, dk, dv, ring_cap, num_slots;
     rs_dtype act_dtype, state_dtype;
+    float scale;
     int32_t tile_v;
 } rs_dims;
 
@@ -106,7 +111,9 @@ typedef struct {
  * write_pos = cursor and the history [0, cursor) is replayed without writing S.  The T
  * draft records go to ring rows [write_pos, write_pos + T).  Causal terms are selected,
  * never multiplied by zero, so non-finite inputs at draft t reach no output before t.
- * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_LAUNCH.
+ *   out[t] = dims->scale * S_t^T q_t, S_t the state after draft t.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_VALUE,
+ * RS_E_LAUNCH.
  */
 rs_status rs_gdn_verify(const rs_dims* dims,
                         const void* q, const void* k, const void* v,
@@ -235,8 +242,10 @@ rs_status rs_materialize(const rs_dims* dims, int is_kda, const void* state,
  *               (bf16: round-to-nearest-even); caller-owned, written by the verify
  *   accept_len  [B] int32 in [0, T]; 0 leaves the state as it is
  * Null rows (slot < 0) are skipped by both.  dims->ring_cap must still be >= T (the
- * dims are shared with the ring calls); dims->tile_v = 0 or a width up to 64.
- * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_LAUNCH.
+ * dims are shared with the ring calls); dims->tile_v = 0 or a width up to 64; outputs are
+ * scaled by dims->scale as in rs_gdn_verify.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_RING_TOO_SMALL, RS_E_VALUE (verify),
+ * RS_E_LAUNCH.
  */
 rs_status rs_snapshot_verify(const rs_dims* dims, int is_kda, const void* q, const void* k,
                              const void* v, const void* beta, const void* gate,

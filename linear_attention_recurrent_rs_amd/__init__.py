@@ -38,12 +38,20 @@ class RSError(RuntimeError):
 
 
 class Dims(ctypes.Structure):
-    """rs_dims: batch, T, hk, hv, dk, dv, ring_cap, num_slots, act_dtype, state_dtype, tile_v."""
+    """rs_dims: batch, T, hk, hv, dk, dv, ring_cap, num_slots, act_dtype, state_dtype,
+    scale, tile_v (the C field order).  Built as Dims(batch, T, hk, hv, dk, dv, ring_cap,
+    num_slots, act_dtype, state_dtype, tile_v=0, scale=1.0): the query scale is a keyword,
+    1.0 unless given."""
     _fields_ = [('batch', ctypes.c_int32), ('T', ctypes.c_int32), ('hk', ctypes.c_int32),
                 ('hv', ctypes.c_int32), ('dk', ctypes.c_int32), ('dv', ctypes.c_int32),
                 ('ring_cap', ctypes.c_int32), ('num_slots', ctypes.c_int32),
                 ('act_dtype', ctypes.c_int), ('state_dtype', ctypes.c_int),
-                ('tile_v', ctypes.c_int32)]
+                ('scale', ctypes.c_float), ('tile_v', ctypes.c_int32)]
+
+    def __init__(self, batch=0, T=1, hk=1, hv=1, dk=16, dv=16, ring_cap=1, num_slots=1,
+                 act_dtype=0, state_dtype=0, tile_v=0, scale=1.0):
+        super().__init__(batch, T, hk, hv, dk, dv, ring_cap, num_slots, act_dtype,
+                         state_dtype, scale, tile_v)
 
     def __repr__(self):
         return 'Dims(' + ', '.join(f'{f}={getattr(self, f)}' for f, _ in self._fields_) + ')'

@@ -1,5 +1,7 @@
 // C ABI of the ReplaySSM library: host-side validation, tile choice and kernel launch.
 // Every entry point enqueues on the caller's stream and returns without synchronising.
+#include <cmath>
+
 #include "rs.h"
 #include "rs_internal.h"
 #include "rs_snapshot.h"
@@ -26,6 +28,9 @@ rs_status check_common(const rs_dims* d, bool need_T) {
   }
   return RS_OK;
 }
+
+// The query scale the verifies apply to their outputs: finite and nonzero.
+bool scale_ok(const rs_dims* d) { return std::isfinite(d->scale) && d->scale != 0.f; }
 
 int tmax_of(int T) {
   int t = 1;
@@ -59,6 +64,7 @@ rs_status verify_plan(const rs_dims* d, bool kda, VerifyPlan* p) {
   rs_status st = check_common(d, true);
   if (st != RS_OK) return st;
   if (kda && d->hv != d->hk) return RS_E_SHAPE;
+  if (!scale_ok(d)) return RS_E_VALUE;
   p->bv = choose_bv(d);
   // a bf16 state tile of 64 columns is only 16 KB: the fast verify takes whole 128-column
   // rows then, so that a workgroup moves as many bytes as an fp32 tile of 64 columns
@@ -99,7 +105,7 @@ rs_status verify_impl(bool kda, const rs_dims* d, const int32_t* cu_seqlens, int
   rs::VerifyArgs a{};
   a.B = d->batch; a.T = d->T; a.hk = d->hk; a.hv = d->hv; a.dk = d->dk; a.dv = d->dv;
   a.L = d->ring_cap; a.G = d->hv / d->hk; a.NV = d->dv / bv; a.num_slots = d->num_slots;
-  a.nblocks = d->batch * d->hv * a.NV;
+  a.nblocks = d->batch * d->hv * a.NV; a.scale = d->scale;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate;
   a.state = state; a.ring_k = ring_k; a.ring_d = ring_d; a.ring_g = ring_g;
   a.cursor = cursor; a.slot_idx = slot_idx; a.out = out; a.write_pos_out = write_pos_out;
@@ -284,6 +290,7 @@ rs_status rs_snapshot_verify(const rs_dims* dims, int is_kda, const void* q, con
   if (st != RS_OK) return st;
   const bool kda = is_kda != 0;
   if (kda && dims->hv != dims->hk) return RS_E_SHAPE;
+  if (!scale_ok(dims)) return RS_E_VALUE;
   int bv = dims->tile_v ? dims->tile_v : (dims->dv % 64 == 0 ? 64 : dims->dv % 32 == 0 ? 32 : 16);
   if (bv > 64) bv = 64;
   if (dims->dv % bv != 0 || rs::snapshot_lds_bytes(dims->dk, bv) > kMaxLds) return RS_E_SHAPE;
@@ -294,6 +301,7 @@ rs_status rs_snapshot_verify(const rs_dims* dims, int is_kda, const void* q, con
   a.B = dims->batch; a.T = dims->T; a.hk = dims->hk; a.hv = dims->hv; a.dk = dims->dk;
   a.dv = dims->dv; a.G = dims->hv / dims->hk; a.NV = dims->dv / bv;
   a.nblocks = dims->batch * dims->hv * a.NV; a.num_slots = dims->num_slots;
+  a.scale = dims->scale;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate; a.state = state;
   a.snapshots = snapshots; a.slot_idx = slot_idx; a.out = out;
   return rs::launch_snapshot_verify(kda, dims->act_dtype == RS_BF16, dims->state_dtype == RS_BF16,
@@ -322,6 +330,7 @@ const char* rs_status_str(rs_status s) {
     case RS_E_DTYPE: return "RS_E_DTYPE: unsupported dtype";
     case RS_E_RING_TOO_SMALL: return "RS_E_RING_TOO_SMALL: ring_cap < T";
     case RS_E_LAUNCH: return "RS_E_LAUNCH: kernel launch failed";
+    case RS_E_VALUE: return "RS_E_VALUE: a scalar argument is out of range (scale)";
   }
   return "unknown rs_status";
 }

@@ -30,6 +30,7 @@ struct LdsLayout {
 
 struct VerifyArgs {
   int B, T, hk, hv, dk, dv, L, G, NV, nblocks, num_slots;
+  float scale;              // query scale of the outputs (fills the padding before q)
   const void* q;
   const void* k;
   const void* v;

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a, RowWindo
         float o = P[t * BV + c];
 #pragma unroll
         for (int u = 0; u <= t; ++u) o = fmaf(Qm[t * TMAX + u], d[u], o);
-        a.out[((tok0 + t) * hv + h) * dv + col] = o;
+        a.out[((tok0 + t) * hv + h) * dv + col] = o * a.scale;
         a.ring_d[(((size_t)slot * L + base + t) * hv + h) * dv + col] = d[t];
       }
     }

@@ -8,6 +8,7 @@ namespace rs {
 
 struct SnapArgs {
   int B, T, hk, hv, dk, dv, G, NV, nblocks, num_slots;
+  float scale;              // query scale of the outputs
   const void* q;
   const void* k;
   const void* v;

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void snapshot_verify_kernel(SnapArgs a) {
     if (tid < BV) {
       float o = 0.f;
       for (int j = 0; j < NG; ++j) o += part[j * BV + tid];
-      a.out[(tok * hv + h) * dv + col0 + tid] = o;
+      a.out[(tok * hv + h) * dv + col0 + tid] = o * a.scale;
     }
     __syncthreads();                 // k, q, gates and partials are rewritten next token
   }

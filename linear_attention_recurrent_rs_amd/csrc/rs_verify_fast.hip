@@ -1016,7 +1016,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         float o = Pv[2 * t];
 #pragma unroll
         for (int u = 0; u <= t; ++u) o = fmaf(Qm[t * TMAX + u], d[u], o);
-        a.out[((tok0 + t) * hv + h) * dv + col] = o;
+        a.out[((tok0 + t) * hv + h) * dv + col] = o * a.scale;
         a.ring_d[(((size_t)slot * L + base + t) * hv + h) * dv + col] = d[t];
       }
     }

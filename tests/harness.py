@@ -87,6 +87,11 @@ def step_data(cfg: W.Config, j: int):
     return acc, ins, pol, next_T
 
 
+def step_force_mask(cfg: W.Config, j: int):
+    """The FORCE commit's per-row mask of step j (None: every live row)."""
+    return W.force_mask(cfg, j)
+
+
 # ----------------------------------------------------------------------------- GPU side
 
 class DeviceRun:
@@ -95,7 +100,8 @@ class DeviceRun:
         self.rs, self.cfg, self.dev = rs, cfg, dev
         self.d = rs.Dims(cfg.B, cfg.T, cfg.hk, cfg.hv, cfg.dk, cfg.dv, cfg.L, cfg.num_slots,
                          rs.BF16 if cfg.act_dtype == 'bf16' else rs.F32,
-                         rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, tile_v)
+                         rs.BF16 if cfg.state_dtype == 'bf16' else rs.F32, tile_v,
+                         scale=cfg.scale32)
         self.slots = torch.from_numpy(init.slots.astype(np.int32)).to(dev)
         self.cursor = torch.from_numpy(init.cursor.astype(np.int32)).to(dev)
         self.fold_len = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
@@ -178,13 +184,13 @@ class DeviceRun:
                             self.rg[layer], self.cursor, self.slots, out)
         return out
 
-    def step(self, acc, ins, pol, next_T, clean=False, lens=None):
+    def step(self, acc, ins, pol, next_T, clean=False, lens=None, force_mask=None):
         self.set_windows(lens)
         outs, wps = [], []
         for layer in range(self.cfg.layers):
             o, w = self.verify(layer, self.inputs_dev(ins[layer], clean))
             outs.append(o); wps.append(w)
-        self.advance(acc, pol, next_T)
+        self.advance(acc, pol, next_T, force_mask)
         if pol != W.FOLD_NONE:
             for layer in range(self.cfg.layers):
                 self.commit(layer)
@@ -202,10 +208,11 @@ class OracleRun:
         self.cursor = init.cursor.copy()
         self.fold_len = np.zeros(cfg.num_slots, np.int32)
         self.layers = [rp.ReplayLayer(init.S[l], init.rk[l], init.rd[l], init.rg[l], cfg.kda,
-                                      cfg.G, cfg.L, slots=tracked) for l in range(cfg.layers)]
+                                      cfg.G, cfg.L, slots=tracked, scale=cfg.scale32)
+                       for l in range(cfg.layers)]
         self.streams = [rp.TokenStream.from_replay(ly, self.cursor) for ly in self.layers]
 
-    def step(self, acc, ins, pol, next_T, with_stream=True, lens=None):
+    def step(self, acc, ins, pol, next_T, with_stream=True, lens=None, force_mask=None):
         outs, wps = [], []
         for l, ly in enumerate(self.layers):
             o, w = rp.verify(ly, self.cursor, self.slots, ins[l], rows=self.rows, lens=lens)
@@ -217,7 +224,7 @@ class OracleRun:
                     fin = np.isfinite(o[r])
                     assert rel_err(o[r][fin], o2[r][fin]) < 1e-9, 'oracle models disagree'
         rp.cursor_advance(self.cursor, self.fold_len, self.slots, acc, self.cfg.T, self.cfg.L,
-                          pol, next_T, lens=lens)
+                          pol, next_T, force_mask, lens=lens)
         for ly in self.layers:
             rp.commit_fold(ly, self.fold_len, self.slots, rows=self.rows)
         if with_stream:
@@ -234,6 +241,8 @@ class StepReport:
     state_err: float = 0.0
     ring_d_err: float = 0.0
     ints_exact: bool = True
+    commit_folds: int = 0        # (row, step) pairs a folding policy folded at commit
+    commit_stays: int = 0        # (row, step) pairs a folding policy left unfolded
 
 
 def compare_step(cfg: W.Config, g: DeviceRun, o: OracleRun, g_outs, g_wps, o_outs, o_wps, acc,

@@ -41,14 +41,20 @@ def _run(cfg, rows=None, steps=None, tile_v=0):
     for j in range(cfg.steps if steps is None else steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
         lens = H.step_windows(cfg, j)
-        print(f'[{cfg.name}] step {j} policy {pol}' +
-              ('' if lens is None else f' windows {lens.tolist()}'), flush=True)
-        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens)
-        o_outs, o_wps = o.step(acc, ins, pol, next_T, lens=lens)
+        fm = H.step_force_mask(cfg, j)
+        print(f'[{cfg.name}] step {j} policy {pol} next_T {next_T}' +
+              ('' if lens is None else f' windows {lens.tolist()}') +
+              ('' if fm is None else f' force_mask {fm.tolist()}'), flush=True)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens, force_mask=fm)
+        o_outs, o_wps = o.step(acc, ins, pol, next_T, lens=lens, force_mask=fm)
         rep = H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, acc, rows, init)
         worst.out_err = max(worst.out_err, rep.out_err)
         worst.state_err = max(worst.state_err, rep.state_err)
         worst.ring_d_err = max(worst.ring_d_err, rep.ring_d_err)
+        if pol != W.FOLD_NONE:
+            live_s = [int(init.slots[r]) for r in rows if init.slots[r] >= 0]
+            worst.commit_folds += sum(int(o.fold_len[s] > 0) for s in live_s)
+            worst.commit_stays += sum(int(o.fold_len[s] == 0) for s in live_s)
     H.check_untouched(cfg, g, init)
     # the accepted state, read-only
     for l in range(cfg.layers):
@@ -87,6 +93,56 @@ def test_c0_against_golden():
 @pytest.mark.parametrize('name', sorted(REDUCED))
 def test_reduced_all_rows(name):
     _run(REDUCED[name])
+
+
+# ----------------------------------------------------------------------------- fold policies
+# The lazy policy (fold at commit when the next verify, of width next_T, would overflow;
+# next_T alternates between T and T + 1) and FORCE with a seeded per-row mask, on the
+# large-ring shapes (ring 64, window 8, 4 layers sharing one cursor) and on an fp32-state
+# decode with staggered cursors.
+
+POLICIES = {
+    'large_ring_lazy': REDUCED['c4'].with_(policy='lazy', steps=24),
+    'large_ring_force_mask': REDUCED['c4'].with_(policy='force_mask', force_p=0.4, steps=16),
+    'decode_lazy': REDUCED['c1'].with_(policy='lazy', steps=24),
+    'decode_force_mask': REDUCED['c1'].with_(policy='force_mask', force_p=0.3, steps=20),
+    'decode_T3_lazy': REDUCED['c1'].with_(T=3, accept=('uniform', 0, 3), policy='lazy',
+                                          steps=16),
+}
+
+
+@pytest.mark.parametrize('name', sorted(POLICIES))
+def test_fold_policies(name):
+    """LAZY and per-row FORCE through rs_cursor_advance and rs_commit_fold: cursors and
+    fold_len bit-exact against the oracle every step, outputs, states and ring deltas at
+    tolerance.  Some rows must fold at commit and some must not."""
+    cfg = POLICIES[name]
+    _, _, _, worst = _run(cfg)
+    print(f'[{name}] commit folds {worst.commit_folds}, rows left unfolded {worst.commit_stays}')
+    assert worst.commit_folds > 0 and worst.commit_stays > 0
+
+
+# ----------------------------------------------------------------------------- decode, T = 3
+# The benchmark's second window width: fp32 state, 64-column tiles, window 3 (the readout
+# on bf16 MFMAs over the state split into high and low parts, the fused fold on bf16 MFMAs,
+# six workgroups per CU), staggered cursors so that every launch mixes history lengths
+# 0..13 with rows folding in-verify.
+
+def test_decode_T3_all_rows():
+    cfg = REDUCED['c1'].with_(T=3, accept=('uniform', 1, 3), steps=24)
+    _run(cfg)
+
+
+@pytest.mark.parametrize('scale_name', ['rsqrt_dk', 'two'])
+def test_query_scale(scale_name):
+    """A query scale other than 1 (dk^-1/2 as the usual attention scale, and 2): outputs
+    scaled, states and rings as at scale 1, on the fp32 decode at T = 3, the bf16 spec
+    verify and KDA."""
+    sc = 128 ** -0.5 if scale_name == 'rsqrt_dk' else 2.0
+    _run(REDUCED['c1'].with_(T=3, accept=('uniform', 1, 3), steps=10, scale=sc))
+    _run(REDUCED['c2'].with_(steps=6, scale=sc))
+    _run(REDUCED['c3'].with_(steps=6, scale=sc))
+    _run(W.CONFIGS['c0'].with_(steps=8, scale=sc))        # the general kernels
 
 
 @pytest.mark.parametrize('tile_v', [16, 32, 128])

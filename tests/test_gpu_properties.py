@@ -165,9 +165,11 @@ def _sampled(cfg, rows, steps):
     for j in range(steps):
         acc, ins, pol, next_T = H.step_data(cfg, j)
         lens = H.step_windows(cfg, j)
-        print(f'[{cfg.name} full] step {j}', flush=True)
-        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens)
-        o_outs, o_wps = o.step(acc, ins, pol, next_T, with_stream=False, lens=lens)
+        fm = H.step_force_mask(cfg, j)
+        print(f'[{cfg.name} full] step {j} policy {pol}', flush=True)
+        g_outs, g_wps = g.step(acc, ins, pol, next_T, lens=lens, force_mask=fm)
+        o_outs, o_wps = o.step(acc, ins, pol, next_T, with_stream=False, lens=lens,
+                               force_mask=fm)
         rep = H.compare_step(cfg, g, o, g_outs, g_wps, o_outs, o_wps, acc, rows, init)
         worst.out_err = max(worst.out_err, rep.out_err)
         worst.state_err = max(worst.state_err, rep.state_err)
@@ -190,6 +192,28 @@ def test_full_size_decode_sampled():
     staggered cursors): 18 steps so that every row folds in-verify at least once."""
     cfg = W.CONFIGS['c1'].with_(steps=18)
     _sampled(cfg, _rows(cfg, 5), cfg.steps)
+
+
+def test_full_size_decode_T3_sampled():
+    """The benchmark's T = 3 workload at full size (64 rows, fp32 state, ring 16, accept
+    U{1..3}, staggered cursors): 32 steps, so rows replay 0..13 history records and fold
+    in-verify repeatedly, in the launch configuration the benchmark times (the key-group
+    XCD order, six workgroups per CU)."""
+    cfg = W.CONFIGS['c1'].with_(T=3, accept=('uniform', 1, 3), steps=32)
+    _sampled(cfg, _rows(cfg, 5), cfg.steps)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_large_ring_sampled():
+    """The large-ring workload at full size: 256 rows, 16/32 heads, ring 64, window 8,
+    4 layers sharing one cursor array, Binomial(8, 0.7) accepts; fused folds only for 16
+    steps, then a forced commit fold of every row every third step (steps 16 and 19 here;
+    batch x key heads a multiple of 8, so the verify takes the key-group XCD order).  The
+    fp64 oracle replays up to 64 history records per sampled row, layer and step, so the
+    sample is three rows over 20 steps."""
+    cfg = W.CONFIGS['c4'].with_(steps=20)
+    assert (cfg.B * cfg.hk) % 8 == 0
+    _sampled(cfg, _rows(cfg, 3), cfg.steps)
 
 
 def test_full_size_spec_verify_sampled():

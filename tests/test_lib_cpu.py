@@ -32,15 +32,39 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = rs._lib()
-    for code in range(6):
+    for code in range(7):
         assert lib.rs_status_str(code).decode().startswith('RS_')
 
 
 def _dims(**kw):
     d = dict(batch=4, T=1, hk=2, hv=4, dk=128, dv=128, ring_cap=16, num_slots=8,
-             act_dtype=rs.BF16, state_dtype=rs.F32, tile_v=0)
+             act_dtype=rs.BF16, state_dtype=rs.F32, tile_v=0, scale=1.0)
     d.update(kw)
-    return rs.Dims(*[d[f] for f, _ in rs.Dims._fields_])
+    return rs.Dims(**d)
+
+
+def test_dims_layout():
+    """The Python struct matches rs_dims: the query scale sits between the dtypes and the
+    tile width, and defaults to 1."""
+    assert [f for f, _ in rs.Dims._fields_][-2:] == ['scale', 'tile_v']
+    assert ctypes.sizeof(rs.Dims) == 12 * 4
+    d = rs.Dims(1, 2, 3, 4, 16, 32, 8, 9, rs.BF16, rs.F32, 64)
+    assert (d.tile_v, d.scale, d.dv) == (64, 1.0, 32)
+    assert rs.Dims(1, 1, 1, 1, 16, 16, 4, 1, scale=0.125).scale == 0.125
+
+
+@pytest.mark.parametrize('scale', [0.0, float('nan'), float('inf'), -float('inf')])
+def test_scale_validation(scale):
+    """The verifies refuse a query scale that is zero or not finite (RS_E_VALUE = 6), on
+    the host before any launch; the commit fold and materialize do not read it."""
+    lib = rs._lib()
+    d = _dims(scale=scale)
+    fake = ctypes.c_void_p(256)
+    assert lib.rs_gdn_verify(ctypes.byref(d), *([fake] * 14), None) == 6
+    assert lib.rs_kda_verify(ctypes.byref(_dims(scale=scale, hk=4)), *([fake] * 14), None) == 6
+    assert lib.rs_snapshot_verify(ctypes.byref(d), 0, *([fake] * 9), None) == 6
+    assert lib.rs_verify_launch_info(ctypes.byref(d), 0, None, None, None) == 6
+    assert lib.rs_commit_fold(ctypes.byref(d), 0, *([None] * 6), None) == 1   # NULLPTR, not VALUE
 
 
 @pytest.mark.parametrize('kw,code', [

@@ -47,14 +47,21 @@ class Config:
     seed: int = 0
     nan_frac: float = 0.0        # probability a rejected position gets a non-finite v entry
     cursor_init: str = 'zero'    # 'zero' | 'stagger' (cursor = row mod L, ring prefilled)
-    policy: str = 'none'         # 'none' | 'every_commit' | 'c4_schedule'
+    policy: str = 'none'         # 'none' | 'every_commit' | 'lazy' | 'force_mask' | 'c4_schedule'
     extra_slots: int = 16
     ragged: tuple = ()           # () = every row verifies T tokens; ('uniform', lo, hi) =
                                  # per-row window widths U{lo..hi} (packed token list)
+    scale: float = 1.0           # query scale of the outputs, o = scale S^T q
+    force_p: float = 0.0         # 'force_mask' policy: probability a row is masked in
 
     @property
     def G(self) -> int:
         return self.hv // self.hk
+
+    @property
+    def scale32(self) -> float:
+        """The query scale as the fp32 value the library receives."""
+        return float(np.float32(self.scale))
 
     @property
     def num_slots(self) -> int:
@@ -107,11 +114,18 @@ def step_policy(cfg: Config, step: int):
 
     c4_schedule: steps 0-15 rely on the fused in-verify fold only; from step 16 on, every
     third step forces a commit fold of every live row (the force_compress switch).
+    lazy: fold at commit when the next verify would overflow; the next window width
+    alternates between T and T + 1 (capped at 16), so the policy must read next_T, not T.
+    force_mask: FORCE with a seeded per-row mask every step (``force_mask``).
     """
     if cfg.policy == 'none':
         return FOLD_NONE, cfg.T
     if cfg.policy == 'every_commit':
         return FOLD_EVERY_COMMIT, cfg.T
+    if cfg.policy == 'lazy':
+        return FOLD_LAZY, min(cfg.T + (step % 2), 16)
+    if cfg.policy == 'force_mask':
+        return FOLD_FORCE, cfg.T
     if cfg.policy == 'c4_schedule':
         if step >= 16 and (step - 16) % 3 == 0:
             return FOLD_FORCE, cfg.T
@@ -147,7 +161,7 @@ def _rng(cfg: Config, *purpose: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([cfg.seed, *purpose]))
 
 
-_P_SLOTS, _P_STATE, _P_RING, _P_TOKENS, _P_ACCEPT, _P_NAN, _P_WINDOW = 1, 2, 3, 4, 5, 6, 7
+_P_SLOTS, _P_STATE, _P_RING, _P_TOKENS, _P_ACCEPT, _P_NAN, _P_WINDOW, _P_FORCE = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _unit(rng, shape):
@@ -215,6 +229,15 @@ def initial_ring(cfg: Config, cursor: np.ndarray, layer: int = 0, fill=np.nan):
         rd[s, :c] = to_f32(0.5 * rng.standard_normal((c, cfg.hv, cfg.dv)))
         rg[s, :c] = to_dtype(_gate(rng, (c,) + gshape[2:]), cfg.act_dtype)
     return rk, rd, rg
+
+
+def force_mask(cfg: Config, step: int) -> Optional[np.ndarray]:
+    """uint8 [B]: the rows a FORCE commit folds at ``step`` under the 'force_mask' policy
+    (each row masked in with probability force_p), else None (every live row)."""
+    if cfg.policy != 'force_mask':
+        return None
+    rng = _rng(cfg, _P_FORCE, step)
+    return (rng.random(cfg.B) < cfg.force_p).astype(np.uint8)
 
 
 def window_lengths(cfg: Config, step: int) -> Optional[np.ndarray]:
