@@ -61,7 +61,8 @@ typedef enum {
     RS_E_DTYPE = 3,           /* unsupported dtype */
     RS_E_RING_TOO_SMALL = 4,  /* ring_cap < T: the ring cannot hold the draft window */
     RS_E_LAUNCH = 5,          /* the kernel launch failed (hipGetLastError) */
-    RS_E_VALUE = 6            /* a scalar argument is out of range (dims->scale) */
+    RS_E_VALUE = 6,           /* a scalar argument is out of range (dims->scale) */
+    RS_E_SCRATCH = 7          /* too large for rs_gdn_verify_noalloc's static workspace */
 } rs_status;
 
 typedef enum { RS_F32 = 0, RS_BF16 = 1 } rs_dtype;
@@ -122,6 +123,24 @@ rs_status rs_gdn_verify(const rs_dims* dims,
                         const int32_t* cursor, const int32_t* slot_idx,
                         float* out, int32_t* write_pos_out, int32_t* group_counter,
                         hipStream_t stream);
+
+/*
+ * rs_gdn_verify_noalloc -- rs_gdn_verify for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without group_counter, the same kernels and the same results.  The
+ * fold counters it needs live in a static device array inside the library, 65536 int32
+ * (256 KiB) on each GPU the library runs on, held until the process ends; the call clears
+ * the batch * hk counters it uses (a fill kernel on the stream) and allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls whose executions overlap on one
+ * GPU (concurrent streams, or host threads) race on it and must be ordered by the caller.
+ * Errors: as rs_gdn_verify; RS_E_SCRATCH when batch * hk > 65536.
+ */
+rs_status rs_gdn_verify_noalloc(const rs_dims* dims,
+                                const void* q, const void* k, const void* v,
+                                const void* beta, const void* gate,
+                                void* state, void* ring_k, float* ring_d, float* ring_g,
+                                const int32_t* cursor, const int32_t* slot_idx,
+                                float* out, int32_t* write_pos_out, hipStream_t stream);
 
 /*
  * rs_kda_verify -- as rs_gdn_verify for KDA (LightLLM: KDA gets the same windowed

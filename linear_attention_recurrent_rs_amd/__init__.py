@@ -22,7 +22,7 @@ __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'com
            'prepare_verify_varlen', 'prepare_cursor_advance_varlen',
            'materialize', 'verify_launch_info', 'stream_read', 'library_path', 'F32', 'BF16',
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
-           'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE']
+           'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE', 'gdn_verify_noalloc']
 
 F32, BF16 = 0, 1
 FOLD_NONE, FOLD_EVERY_COMMIT, FOLD_LAZY, FOLD_FORCE = 0, 1, 2, 3
@@ -77,6 +77,8 @@ def _lib():
         for name in ('rs_gdn_verify_varlen', 'rs_kda_verify_varlen'):
             getattr(lib, name).argtypes = varlen_args
             getattr(lib, name).restype = ctypes.c_int
+        lib.rs_gdn_verify_noalloc.argtypes = [dp] + [_P] * 13 + [_P]
+        lib.rs_gdn_verify_noalloc.restype = ctypes.c_int
         lib.rs_cursor_advance.argtypes = [dp, _P, _P, _P, _P, ctypes.c_int, ctypes.c_int32, _P, _P]
         lib.rs_cursor_advance.restype = ctypes.c_int
         lib.rs_cursor_advance_varlen.argtypes = [dp, _P, ctypes.c_int32, _P, _P, _P, _P,
@@ -128,7 +130,8 @@ def _check(status: int, where: str):
 
 
 def _verify_ptrs(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
-                 slot_idx, out, write_pos_out, group_counter, ntok=None):
+                 slot_idx, out, write_pos_out, group_counter, ntok=None,
+                 counter_optional=False):
     at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
     BT = d.batch * d.T if ntok is None else ntok
     S, L = d.num_slots, d.ring_cap
@@ -144,7 +147,8 @@ def _verify_ptrs(kda: bool, d: Dims, q, k, v, beta, gate, state, ring_k, ring_d,
         _ptr(cursor, 'cursor', S, torch.int32), _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
         _ptr(out, 'out', BT * d.hv * d.dv, torch.float32),
         _ptr(write_pos_out, 'write_pos_out', d.batch, torch.int32, optional=True),
-        _ptr(group_counter, 'group_counter', d.batch * d.hk, torch.int32),
+        _ptr(group_counter, 'group_counter', d.batch * d.hk, torch.int32,
+             optional=counter_optional),
     ]
     return args
 
@@ -162,6 +166,16 @@ def gdn_verify(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, curs
     """rs_gdn_verify: one GDN layer's verify (decode when T == 1)."""
     _verify(False, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx, out,
             write_pos_out, group_counter, stream)
+
+
+def gdn_verify_noalloc(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                       slot_idx, out, write_pos_out=None, stream=None):
+    """rs_gdn_verify_noalloc: rs_gdn_verify with the fold counters in the library's static
+    device workspace (no group_counter argument; nothing is allocated)."""
+    args = _verify_ptrs(False, d, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor,
+                        slot_idx, out, write_pos_out, None, counter_optional=True)
+    _check(_lib().rs_gdn_verify_noalloc(ctypes.byref(d), *args[:-1], _stream(stream)),
+           'rs_gdn_verify_noalloc')
 
 
 def kda_verify(d: Dims, q, k, v, beta, gate, state, ring_k, ring_d, ring_g, cursor, slot_idx,

@@ -226,6 +226,24 @@ rs_status rs_kda_verify_varlen(const rs_dims* dims, const int32_t* cu_seqlens,
                      ring_d, ring_g, cursor, slot_idx, out, write_pos_out, group_counter, stream);
 }
 
+rs_status rs_gdn_verify_noalloc(const rs_dims* dims, const void* q, const void* k,
+                                const void* v, const void* beta, const void* gate, void* state,
+                                void* ring_k, float* ring_d, float* ring_g,
+                                const int32_t* cursor, const int32_t* slot_idx, float* out,
+                                int32_t* write_pos_out, hipStream_t stream) {
+  VerifyPlan plan;
+  rs_status st = verify_plan(dims, false, &plan);
+  if (st != RS_OK) return st;
+  if ((int64_t)dims->batch * dims->hk > rs::kNoAllocCounters) return RS_E_SCRATCH;
+  if (dims->batch == 0) return RS_OK;
+  int32_t* counters = nullptr;
+  if (rs::noalloc_counters(&counters) != hipSuccess) return RS_E_LAUNCH;
+  if (rs::launch_zero_counters(counters, dims->batch * dims->hk, stream) != hipSuccess)
+    return RS_E_LAUNCH;
+  return verify_impl(false, dims, nullptr, 0, q, k, v, beta, gate, state, ring_k, ring_d, ring_g,
+                     cursor, slot_idx, out, write_pos_out, counters, stream);
+}
+
 static rs_status advance_impl(const rs_dims* dims, const int32_t* cu_seqlens, int32_t ntok,
                               int32_t* cursor, int32_t* fold_len, const int32_t* slot_idx,
                               const int32_t* accept_len, rs_fold_policy policy, int32_t next_T,
@@ -331,6 +349,8 @@ const char* rs_status_str(rs_status s) {
     case RS_E_RING_TOO_SMALL: return "RS_E_RING_TOO_SMALL: ring_cap < T";
     case RS_E_LAUNCH: return "RS_E_LAUNCH: kernel launch failed";
     case RS_E_VALUE: return "RS_E_VALUE: a scalar argument is out of range (scale)";
+    case RS_E_SCRATCH:
+      return "RS_E_SCRATCH: batch * hk exceeds the allocation-free verify's static workspace";
   }
   return "unknown rs_status";
 }

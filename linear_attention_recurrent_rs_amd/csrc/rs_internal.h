@@ -292,4 +292,12 @@ hipError_t launch_fold_bf16(bool kda, bool materialize, const FoldArgs& a,
                             const FoldFastLayout& lay, hipStream_t s);
 hipError_t launch_advance(const AdvanceArgs& a, hipStream_t s);
 
+// The allocation-free verify's fold counters (rs_noalloc.hip): a file-scope device array of
+// kNoAllocCounters int32 (256 KiB per GPU), so batch * hk <= kNoAllocCounters.
+constexpr int kNoAllocCounters = 65536;
+// Device address of the current device's array (looked up once per device).
+hipError_t noalloc_counters(int32_t** out);
+// Zero the first n counters on the stream (a fill kernel).
+hipError_t launch_zero_counters(int32_t* p, int n, hipStream_t s);
+
 }  // namespace rs

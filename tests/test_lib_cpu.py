@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = rs._lib()
-    for code in range(7):
+    for code in range(8):
         assert lib.rs_status_str(code).decode().startswith('RS_')
 
 
