@@ -17,8 +17,9 @@ value = verified tokens per second per layer = live rows * T * layers / step tim
 roofline: the verify kernel; achieved = algorithmic bytes per launch (from the integer
 cursor model: state read, inputs, history records read, outputs and ring writes, the
 state write of rows that fold) / mean launch time from HIP events on the launch stream
-around each timed step's back-to-back verifies (divided by the layer count).  cpu_baseline: the fp64 oracle on a bounded
-sample of the same workload, single-threaded.
+around each timed step's back-to-back verifies (divided by the layer count).
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload, one process per
+host core (and a single-thread run beside it), with the CPU model.
 
 extra: the T = 3 case; the T = 1 verify at three history states (none, steady, every row
 folding); and full step loops (verify per layer, cursor advance, commit folds by policy)
@@ -216,11 +217,11 @@ def copy_calibration(mib: int = 256, reps: int = 4):
     print(f'# copy calibration: {reps} copies of {mib} MiB', file=sys.stderr, flush=True)
 
 
-def cpu_baseline(T: int, budget_s: float = 12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same decode workload:
-    8 live rows (all 32 value heads, full dk = dv = 128), one layer, consecutive steps
-    until the time budget is spent.  BLAS limited to one thread; the oracle's loops
-    and einsums run in one thread."""
+def _oracle_decode(T: int, rows_pick, budget_s: float, start=None):
+    """The fp64 oracle, as it stands, running consecutive decode steps of one layer of the
+    decode workload for the given live-row indices until budget_s of timed work is spent
+    (input generation is not timed).  BLAS limited to one thread.  Returns (verified
+    tokens, seconds, steps)."""
     from threadpoolctl import threadpool_limits
     import workloads as W
     from oracle import replay as rp
@@ -228,28 +229,73 @@ def cpu_baseline(T: int, budget_s: float = 12.0):
     cfg = W.CONFIGS['c1'].with_(T=T, accept=('const', 1) if T == 1 else ('uniform', 1, T))
     slots = W.slot_map(cfg)
     cursor = W.initial_cursor(cfg, slots)
-    rows = [r for r in range(cfg.B) if slots[r] >= 0][:8]
+    live = [r for r in range(cfg.B) if slots[r] >= 0]
+    rows = [live[i % len(live)] for i in rows_pick]
+    rows = sorted(set(rows))
     rk, rd, rg = W.initial_ring(cfg, cursor, 0)
     layer = rp.ReplayLayer(W.initial_state(cfg, 0), rk, rd, rg, False, cfg.G, cfg.L,
                            slots=[slots[r] for r in rows])
     fl = np.zeros(cfg.num_slots, np.int32)
+    sub = np.full(cfg.B, -1, np.int32)
+    sub[rows] = slots[rows]
     steps, tokens, elapsed = 0, 0, 0.0
+    if start is not None:
+        start.wait()                                   # every worker starts its clock together
     with threadpool_limits(limits=1):
         while elapsed < budget_s:
-            inp = W.step_inputs(cfg, steps, 0)          # input generation is not timed
+            inp = W.step_inputs(cfg, steps, 0)
             acc = W.accept_lengths(cfg, steps)
-            sub = np.full(cfg.B, -1, np.int32)
-            sub[rows] = slots[rows]
             ts = time.perf_counter()
             rp.verify(layer, cursor, slots, inp, rows=rows)
             rp.cursor_advance(cursor, fl, sub, acc, T, cfg.L, rp.FOLD_NONE)
             elapsed += time.perf_counter() - ts
             tokens += len(rows) * T
             steps += 1
-    return {'value': tokens / elapsed, 'unit': 'verified tokens/s per layer', 'cores': 1,
-            'kind': 'oracle',
-            'sample': f'{len(rows)} live rows x 32 value heads (dk=dv=128, ring 16, T={T}), '
-                      f'{steps} decode steps of one layer, {elapsed:.1f} s, fp64 numpy'}
+    return tokens, elapsed, steps
+
+
+def _cpu_model():
+    try:
+        for line in open('/proc/cpuinfo'):
+            if line.startswith('model name'):
+                return line.split(':', 1)[1].strip()
+    except OSError:
+        pass
+    return 'unknown'
+
+
+def cpu_baseline(T: int, budget_s: float = 10.0):
+    """The fp64 oracle on a bounded sample of the decode workload, on the host's cores:
+    one process per core of this process's CPU affinity (at most 16, the host share of one
+    GPU), each running the oracle single-threaded on 4 live rows of its own (all 32 value
+    heads, dk = dv = 128, one layer) for budget_s of timed work, started together; the rate
+    is the sum of the processes' rates.  A single-thread run on 8 live rows is reported
+    beside it.  Runs before anything initialises the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    single = _oracle_decode(T, range(8), budget_s)
+    ctx = mp.get_context('fork')
+    start = ctx.Barrier(n)
+    q = ctx.Queue()
+
+    def work(i):
+        q.put(_oracle_decode(T, range(4 * i, 4 * i + 4), budget_s, start))
+
+    procs = [ctx.Process(target=work, args=(i,)) for i in range(n)]
+    for p in procs:
+        p.start()
+    res = [q.get() for _ in procs]
+    for p in procs:
+        p.join()
+    rate = sum(t / e for t, e, _ in res)
+    return {'value': rate, 'unit': 'verified tokens/s per layer', 'cores': n, 'kind': 'oracle',
+            'cpu_model': _cpu_model(), 'host_cpus': os.cpu_count(),
+            'sample': f'{n} processes x 4 live rows x 32 value heads (dk=dv=128, ring 16, '
+                      f'T={T}), {sum(x[2] for x in res)} decode steps of one layer in all, '
+                      f'{budget_s:.0f} s each, fp64 numpy, one thread per process',
+            'single_thread': {'value': round(single[0] / single[1], 2), 'cores': 1,
+                              'sample': f'8 live rows x 32 value heads, {single[2]} decode '
+                                        f'steps of one layer, {single[1]:.1f} s'}}
 
 
 # ----------------------------------------------------------------------------- more workloads
@@ -361,16 +407,81 @@ def stream_reference(nbytes, pools=8, iters=48):
     return {'bytes': n * 4, 'us': round(us, 3), 'gbs': round(n * 4 / us / 1e3, 1)}
 
 
-def run_workload(name, steps=30, warmup=10, tile_v=0):
+def _bytes_of(cfg):
+    """Per-row byte terms of one layer: state, window inputs per token, history record,
+    writes per token (outputs, ring keys, deltas, gates)."""
+    a = 2 if cfg.act_dtype == 'bf16' else 4
+    s = 2 if cfg.state_dtype == 'bf16' else 4
+    g_in = cfg.hv * cfg.dk * a if cfg.kda else cfg.hv * a
+    g_ring = cfg.hv * cfg.dk * 4 if cfg.kda else cfg.hv * 4
+    return dict(S=cfg.hv * cfg.dk * cfg.dv * s,
+                tok_in=2 * cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * a + cfg.hv * a + g_in,
+                record=cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * 4 + g_ring,
+                tok_out=cfg.hv * cfg.dv * 4 + cfg.hk * cfg.dk * a + cfg.hv * cfg.dv * 4 + g_ring)
+
+
+class CursorModel:
+    """The cursor advance on the host (every policy, uniform or ragged windows), for the
+    algorithmic bytes of each verify and commit-fold launch; the device cursors must end
+    equal to it."""
+
+    def __init__(self, cfg, slots, cursor):
+        self.cfg, self.slots, self.cursor = cfg, slots, cursor.copy()
+        self.b = _bytes_of(cfg)
+
+    def step(self, acc, policy, next_T, lens=None, force_mask=None):
+        """Returns (verify bytes of one layer, commit-fold bytes of one layer) and advances."""
+        c, b = self.cfg, self.b
+        vb = cb = 0
+        for r, s in enumerate(self.slots):
+            if s < 0:
+                continue
+            T = c.T if lens is None else int(lens[r])
+            n = int(self.cursor[s])
+            if T == 0:                      # an empty ragged window reads only its indices
+                vb += 8
+                continue
+            fold = n + T > c.L
+            base = 0 if fold else n
+            vb += b['S'] + T * b['tok_in'] + n * b['record'] + T * b['tok_out'] + \
+                (b['S'] if fold else 0) + 8
+            m = base + min(int(acc[r]), T)
+            if policy == 1:
+                fl = m
+            elif policy == 2:
+                fl = m if m + next_T > c.L else 0
+            elif policy == 3:
+                fl = m if (force_mask is None or force_mask[r]) else 0
+            else:
+                fl = 0
+            if fl:
+                cb += 2 * b['S'] + fl * b['record'] + 8
+            self.cursor[s] = 0 if fl else m
+        return vb, cb
+
+
+def _frac(byts, us):
+    return round(byts / us / 1e3 / HBM_PEAK_GBS, 4) if us > 0 else None
+
+
+def run_workload(name, steps=30, warmup=10, tile_v=0, min_pool_bytes=1 << 30):
     """A full step loop of another workload: a verify per layer, the cursor advance, and the
-    commit folds its policy asks for.  Verify and commit-fold kernel times from HIP events;
-    verified tokens/s per layer = live * T * layers / step time; committed tokens/s per
-    layer = accepted tokens / step time."""
+    commit folds its policy asks for.  Layer pools rotate so that their state and rings
+    together exceed the 256 MB Infinity Cache (at least 8 pools and 1 GiB, or the config's
+    own layers when those are already larger).  Kernel times from one pair of HIP events
+    around each step's verifies and one around its commit folds, divided by the layers;
+    algorithmic bytes per launch from the host cursor model; verified tokens/s per layer =
+    verified tokens * layers / step time; committed tokens/s per layer = accepted tokens *
+    layers / step time (as the headline: the rate of a one-layer stack)."""
     import torch
     import linear_attention_recurrent_rs_amd as rs
     import workloads as W
     cfg = W.CONFIGS[name]
-    layers = cfg.layers
+    b = _bytes_of(cfg)
+    ring_bytes = cfg.num_slots * cfg.L * (b['record'])
+    pool = cfg.num_slots * b['S'] + ring_bytes
+    layers = cfg.layers if cfg.layers * pool >= min_pool_bytes else \
+        max(cfg.layers, 8, -(-min_pool_bytes // pool))
     st = _rand_setup(cfg, layers, tile_v=tile_v)
     dev, slots_np, d = st['dev'], st['slots_np'], st['d']
     cursor = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
@@ -384,10 +495,10 @@ def run_workload(name, steps=30, warmup=10, tile_v=0):
     accs = [W.accept_lengths(cfg, j) for j in range(total)]
     acc_d = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in accs]
     pols = [W.step_policy(cfg, j) for j in range(total)]
+    lens = [W.window_lengths(cfg, j) for j in range(total)]
     if cfg.ragged:
         # ragged windows: each step packs its rows' windows (widths drawn per row and step)
         # into the leading rows of the input buffers, with cumulative lengths on the device
-        lens = [W.window_lengths(cfg, j) for j in range(total)]
         cus = [np.concatenate([[0], np.cumsum(x)]).astype(np.int32) for x in lens]
         cu_d = [torch.from_numpy(c).to(dev) for c in cus]
         ntok = [max(int(c[-1]), 1) for c in cus]
@@ -410,28 +521,34 @@ def run_workload(name, steps=30, warmup=10, tile_v=0):
         verified = [len(live) * cfg.T] * total
     commit = [rs.prepare_commit_fold(d, cfg.kda, st['S'][l], st['rk'][l], st['rd'][l],
                                      st['rg'][l], fold_len, st['slots']) for l in range(layers)]
+    model = CursorModel(cfg, slots_np, np.zeros(cfg.num_slots, np.int32))
+    vbytes, cbytes = [], []
+    for j in range(total):
+        v_, c_ = model.step(accs[j], *pols[j], lens=lens[j])
+        vbytes.append(v_)
+        cbytes.append(c_)
     stream = torch.cuda.current_stream()
     ev_v, ev_c = [], []
 
     def step(j, timed):
+        if timed:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
         for l in range(layers):
+            verify[j % len(verify)][l](stream)
+        if timed:
+            e[1].record(stream)
+            ev_v.append(e)
+        adv[j](stream)
+        if pols[j][0] != rs.FOLD_NONE:
             if timed:
                 e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 e[0].record(stream)
-            verify[j % len(verify)][l](stream)
+            for l in range(layers):
+                commit[l](stream)
             if timed:
                 e[1].record(stream)
-                ev_v.append(e)
-        adv[j](stream)
-        if pols[j][0] != rs.FOLD_NONE:
-            for l in range(layers):
-                if timed:
-                    e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    e[0].record(stream)
-                commit[l](stream)
-                if timed:
-                    e[1].record(stream)
-                    ev_c.append(e)
+                ev_c.append((j, e))
 
     for j in range(warmup):
         step(j, False)
@@ -441,40 +558,61 @@ def run_workload(name, steps=30, warmup=10, tile_v=0):
         step(j, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    assert np.array_equal(cursor.cpu().numpy(), model.cursor), 'cursor model diverged'
     step_s = (t1 - t0) / steps
     acc_per_step = float(np.mean([sum(int(accs[j][r]) for r in live) for j in range(warmup, total)]))
+    v_us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev_v])) * 1e3 / layers
+    v_b = float(np.mean(vbytes[warmup:]))
     res = {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'ring': cfg.L, 'layers': layers,
+           'layer_pool_bytes': pool,
            'windows': f'ragged U{{{cfg.ragged[1]}..{cfg.ragged[2]}}}' if cfg.ragged else 'T',
            'kda': cfg.kda, 'state': cfg.state_dtype, 'ms_per_step': round(step_s * 1e3, 5),
            'verified_tokens_per_s_per_layer':
-               round(float(np.mean(verified[warmup:])) / step_s, 1),
-           'committed_tokens_per_s_per_layer': round(acc_per_step / step_s, 1),
-           'verify_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_v])) * 1e3, 3)}
+               round(float(np.mean(verified[warmup:])) * layers / step_s, 1),
+           'committed_tokens_per_s_per_layer': round(acc_per_step * layers / step_s, 1),
+           'verify_us': round(v_us, 3), 'verify_bytes_per_launch': int(v_b),
+           'verify_gbs': round(v_b / v_us / 1e3, 1), 'verify_frac': _frac(v_b, v_us),
+           'verify_bytes_all_steps': int(np.mean(vbytes))}
     if ev_c:
-        res['commit_fold_us'] = round(float(np.mean([a.elapsed_time(b) for a, b in ev_c])) * 1e3, 3)
-        res['commit_folds_per_step'] = round(len(ev_c) / steps, 3)
+        c_us = float(np.mean([e[0].elapsed_time(e[1]) for _, e in ev_c])) * 1e3 / layers
+        c_b = float(np.mean([cbytes[j] for j, _ in ev_c]))
+        res.update({'commit_fold_us': round(c_us, 3), 'commit_bytes_per_launch': int(c_b),
+                    'commit_gbs': round(c_b / c_us / 1e3, 1), 'commit_frac': _frac(c_b, c_us),
+                    'commit_steps': len(ev_c),
+                    'commit_bytes_all_steps': int(np.mean([cbytes[j] for j in range(total)
+                                                            if pols[j][0] != rs.FOLD_NONE]))})
     return res
 
 
-def snapshot_baseline(name='c2', steps=30, warmup=10):
-    """The snapshot-verify baseline on a workload's shapes (one layer): a verify that writes
-    the state after every draft token, then a commit that copies the accepted snapshot into
-    the state, against ReplaySSM's ring of records.  Kernel times from HIP events; memory =
+def snapshot_baseline(name='c2', steps=30, warmup=10, layers=8):
+    """The snapshot-verify baseline on a workload's shapes: per layer a verify that writes
+    the state after every draft token, then, after every layer's verify, a commit per
+    layer that copies the accepted snapshot into the state; against ReplaySSM's ring of
+    records.  8 layer pools (state and snapshots, about 5 GB) rotate, so the Infinity Cache
+    serves none of them.  Kernel times from one pair of HIP events around each step's
+    verifies and one around its commits, divided by the layers; algorithmic bytes: the
+    state read, window inputs, outputs and T snapshot writes per live row (verify); the
+    accepted snapshot read and the state write per row with accept > 0 (commit).  Memory =
     the per-layer buffers each design keeps for the batch."""
     import torch
     import linear_attention_recurrent_rs_amd as rs
     import workloads as W
     cfg = W.CONFIGS[name]
-    st = _rand_setup(cfg, 1)
+    st = _rand_setup(cfg, layers)
     dev, slots_np, d = st['dev'], st['slots_np'], st['d']
     sd = torch.bfloat16 if cfg.state_dtype == 'bf16' else torch.float32
-    snaps = torch.empty(cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv, dtype=sd, device=dev)
+    snaps = [torch.empty(cfg.B, cfg.T, cfg.hv, cfg.dk, cfg.dv, dtype=sd, device=dev)
+             for _ in range(layers)]
     out = torch.empty(cfg.B * cfg.T, cfg.hv, cfg.dv, device=dev)
     sets = [st['inputs']() for _ in range(4)]
     total = warmup + steps
-    accs = [torch.from_numpy(W.accept_lengths(cfg, j).astype(np.int32)).to(dev)
-            for j in range(total)]
+    accs_np = [W.accept_lengths(cfg, j) for j in range(total)]
+    accs = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in accs_np]
     live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+    b = _bytes_of(cfg)
+    v_b = len(live) * (b['S'] + cfg.T * b['tok_in'] + cfg.T * cfg.hv * cfg.dv * 4 +
+                       cfg.T * b['S'] + 8)
+    c_b = [sum(2 * b['S'] + 8 for r in live if accs_np[j][r] > 0) for j in range(total)]
     stream = torch.cuda.current_stream()
     ev_v, ev_c = [], []
 
@@ -482,11 +620,13 @@ def snapshot_baseline(name='c2', steps=30, warmup=10):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
         if timed:
             e[0].record(stream)
-        rs.snapshot_verify(d, cfg.kda, *sets[j % 4], st['S'][0], snaps, st['slots'], out,
-                           stream=stream)
+        for l in range(layers):
+            rs.snapshot_verify(d, cfg.kda, *sets[j % 4], st['S'][l], snaps[l], st['slots'], out,
+                               stream=stream)
         if timed:
             e[1].record(stream)
-        rs.snapshot_commit(d, st['S'][0], snaps, st['slots'], accs[j], stream=stream)
+        for l in range(layers):
+            rs.snapshot_commit(d, st['S'][l], snaps[l], st['slots'], accs[j], stream=stream)
         if timed:
             e[2].record(stream)
             ev_v.append((e[0], e[1]))
@@ -500,19 +640,21 @@ def snapshot_baseline(name='c2', steps=30, warmup=10):
         step(j, True)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / steps
-    acc_sum = float(np.mean([int(accs[j][live].sum()) for j in range(warmup, total)]))
-    s_bytes = 2 if cfg.state_dtype == 'bf16' else 4
-    a_bytes = 2 if cfg.act_dtype == 'bf16' else 4
-    g_ring = cfg.hv * cfg.dk * 4 if cfg.kda else cfg.hv * 4
-    ring = cfg.L * (cfg.hk * cfg.dk * a_bytes + cfg.hv * cfg.dv * 4 + g_ring)
+    acc_sum = float(np.mean([int(accs_np[j][live].sum()) for j in range(warmup, total)]))
+    v_us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev_v])) * 1e3 / layers
+    c_us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev_c])) * 1e3 / layers
+    cb = float(np.mean(c_b[warmup:]))
     return {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'state': cfg.state_dtype,
-            'ms_per_step': round(step_s * 1e3, 5),
-            'verify_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_v])) * 1e3, 3),
-            'commit_us': round(float(np.mean([a.elapsed_time(b) for a, b in ev_c])) * 1e3, 3),
-            'verified_tokens_per_s_per_layer': round(len(live) * cfg.T / step_s, 1),
-            'committed_tokens_per_s_per_layer': round(acc_sum / step_s, 1),
-            'snapshot_bytes_per_layer': cfg.B * cfg.T * cfg.hv * cfg.dk * cfg.dv * s_bytes,
-            'ring_bytes_per_layer': cfg.B * ring}
+            'layers': layers, 'ms_per_step': round(step_s * 1e3, 5),
+            'verify_us': round(v_us, 3), 'verify_bytes_per_launch': int(v_b),
+            'verify_gbs': round(v_b / v_us / 1e3, 1), 'verify_frac': _frac(v_b, v_us),
+            'commit_us': round(c_us, 3), 'commit_bytes_per_launch': int(cb),
+            'commit_gbs': round(cb / c_us / 1e3, 1), 'commit_frac': _frac(cb, c_us),
+            'verified_tokens_per_s_per_layer': round(len(live) * cfg.T * layers / step_s, 1),
+            'committed_tokens_per_s_per_layer': round(acc_sum * layers / step_s, 1),
+            'snapshot_bytes_per_layer': cfg.B * cfg.T * cfg.hv * cfg.dk * cfg.dv * b['S'] //
+                                        (cfg.hv * cfg.dk * cfg.dv),
+            'ring_bytes_per_layer': cfg.B * cfg.L * b['record']}
 
 
 def main():
@@ -545,14 +687,21 @@ def main():
         sys.exit(2)
 
     if args.only_workload:
+        if args.copy_calibration:
+            copy_calibration()
         if args.only_workload.startswith('snapshot_'):
             print(json.dumps(snapshot_baseline(args.only_workload[len('snapshot_'):])), flush=True)
         else:
             print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
         return
+    Ts = [args.only_T] if args.only_T else [1, 3]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # first: its worker processes are forked before anything initialises the GPU
+        cpu = cpu_baseline(Ts[0])
+        print(f'# cpu baseline: {cpu}', file=sys.stderr, flush=True)
     if args.copy_calibration:
         copy_calibration()
-    Ts = [args.only_T] if args.only_T else [1, 3]
     res = {}
     for T in Ts:
         res[T] = run_gpu(T, args.steps, args.warmup, args.layers, args.tile_v)
@@ -612,10 +761,9 @@ def main():
         print(f'# snapshot baseline: {extra["snapshot_baseline_c2"]}', file=sys.stderr, flush=True)
     if extra:
         line['extra'] = extra
-    if not args.no_cpu_baseline:
-        line['cpu_baseline'] = cpu_baseline(Ts[0])
-        cb = line['cpu_baseline']
-        cb['value'] = round(cb['value'], 2)
+    if cpu is not None:
+        cpu['value'] = round(cpu['value'], 2)
+        line['cpu_baseline'] = cpu
     print(json.dumps(line), flush=True)
 
 
