@@ -132,7 +132,7 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   // fold (rs_fold_fast.hip fold_bf16_kernel), when its records fit in LDS
   if (d->state_dtype == RS_BF16 && (d->tile_v == 0 || d->tile_v == 128) && d->dv % 128 == 0 &&
       use_fast(d, 128)) {
-    const rs::FoldFastLayout flay = rs::fold_fast_layout(kda, 128, d->ring_cap);
+    const rs::FoldFastLayout flay = rs::fold_fast_layout(kda, 128, d->ring_cap, false);
     if (flay.total <= kMaxLds) {
       if (d->batch == 0) return RS_OK;
       if (!state_in || !state_out || !ring_k || !ring_d || !ring_g || !nrec || !slot_idx)
@@ -157,7 +157,7 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   rs::LdsLayout lay{};
   for (;;) {
     fast = f32_state && use_fast(d, bv);
-    if (fast) flay = rs::fold_fast_layout(kda, bv, d->ring_cap);
+    if (fast) flay = rs::fold_fast_layout(kda, bv, d->ring_cap, true);
     else lay = rs::fold_layout(kda, dbytes(d->state_dtype), bv, d->dk, d->ring_cap, false);
     const int lds = fast ? flay.total : lay.total;
     if (lds <= kMaxLds || d->tile_v != 0 || bv <= 16) break;

@@ -263,10 +263,12 @@ struct FoldFastLayout {
   int hg;       // gates, fp32 [L] (GDN) or [L x 128] (KDA; then the decayed keys)
   int gam_i;    // GDN: suffix decay of each record [L]
   int Gam;      // KDA: total decay per key channel [128]
+  int stage;    // fp32 fold: per wave 16 rows x (bv + 4) fp32 to write whole row segments,
+                // over the records (dead by then)
   int total;
 };
 
-inline FoldFastLayout fold_fast_layout(bool kda, int bv, int L) {
+inline FoldFastLayout fold_fast_layout(bool kda, int bv, int L, bool stage_rows) {
   auto al = [](int x) { return (x + 15) & ~15; };
   FoldFastLayout l{};
   int o = 0;
@@ -275,7 +277,9 @@ inline FoldFastLayout fold_fast_layout(bool kda, int bv, int L) {
   l.hg = o; o += al(kda ? L * 128 * 4 : L * 4);
   l.gam_i = o; o += kda ? 0 : al(L * 4);
   l.Gam = o; o += kda ? al(128 * 4) : 0;
-  l.total = o;
+  l.stage = 0;
+  const int stage_bytes = stage_rows ? 4 * 16 * (bv + 4) * 4 : 0;   // 4 waves
+  l.total = o > stage_bytes ? o : stage_bytes;
   return l;
 }
 
