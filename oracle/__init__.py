@@ -12,9 +12,13 @@ Contents
                  fold, cursor advance with fold policies, commit fold, materialize) and
                  the token-stream model it is checked against.
   exact       -- exact rational evaluation of the literal dense update, used as a pin.
+  conv        -- the short causal convolution before the recurrence, its per-slot window
+                 state and the rollback of that window at commit, with the token-stream
+                 definition it is checked against.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` (exact rational brute force, closed forms, special cases,
-replay == sequential, fold invariance, exhaustive cursor sequences).
+replay == sequential, fold invariance, exhaustive cursor sequences; the convolution against
+numpy's correlate and scipy's logistic function, exact taps, exhaustive accept sequences).
 """
-from . import delta_rule, replay, exact  # noqa: F401
+from . import conv, delta_rule, replay, exact  # noqa: F401

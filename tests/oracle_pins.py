@@ -13,6 +13,7 @@ from types import SimpleNamespace
 
 import numpy as np
 
+import oracle.conv as cv
 import oracle.delta_rule as dr
 import oracle.replay as rp
 from oracle import exact
@@ -573,8 +574,83 @@ def pin_fold_policies():
         assert folds > 0 and (pol == rp.FOLD_EVERY_COMMIT or stays > 0), (pol, folds, stays)
 
 
+# ----------------------------------------------------------------------------- conv window
+
+
+def pin_conv_correlate():
+    """The conv output against numpy's correlate, channel by channel (tap K-1 on the
+    current input), plus the bias; with SiLU against scipy's logistic function."""
+    from scipy.special import expit
+    rng = np.random.default_rng(26)
+    for K, T, C in ((4, 3, 5), (2, 1, 3), (3, 6, 4)):
+        state = rng.standard_normal((K - 1, C))
+        xw = rng.standard_normal((T, C))
+        w = rng.standard_normal((C, K))
+        b = rng.standard_normal(C)
+        seq = np.concatenate([state, xw])
+        want = np.stack([np.correlate(seq[:, c], w[c], 'valid') for c in range(C)], axis=1) + b
+        got = cv.conv_verify(state, xw, w, b, cv.ACT_NONE)
+        assert _rel(got, want) < 1e-14, ('conv vs correlate', K, T)
+        got = cv.conv_verify(state, xw, w, b, cv.ACT_SILU)
+        assert _rel(got, want * expit(want)) < 1e-14, ('conv silu', K, T)
+        assert np.array_equal(cv.conv_verify(state, xw, w, None, cv.ACT_NONE),
+                              cv.conv_verify(state, xw, w, np.zeros(C), cv.ACT_NONE))
+
+
+def pin_conv_taps():
+    """Tap K-1 alone (no bias, no activation) returns the window inputs exactly; tap 0
+    alone returns the input K-1 positions back, so the first outputs are the state rows,
+    oldest first."""
+    rng = np.random.default_rng(27)
+    K, T, C = 4, 5, 3
+    state = rng.standard_normal((K - 1, C))
+    xw = rng.standard_normal((T, C))
+    w = np.zeros((C, K))
+    w[:, K - 1] = 1.0
+    assert np.array_equal(cv.conv_verify(state, xw, w, None, cv.ACT_NONE), xw)
+    w = np.zeros((C, K))
+    w[:, 0] = 1.0
+    got = cv.conv_verify(state, xw, w, None, cv.ACT_NONE)
+    assert np.array_equal(got, np.concatenate([state, xw])[:T])
+
+
+def pin_conv_rollback_bruteforce():
+    """Every accept sequence over 5 steps with T = 3, K = 4 (4^5 = 1024), and every
+    (window width, accept) sequence over 4 steps with T = 2, K = 3 (6^4 = 1296): after each
+    commit the window state equals, bit for bit, the last K-1 accepted inputs of the
+    token-stream definition, and the window outputs equal the definition's convolution
+    over the whole accepted history; a null row's state never changes."""
+    rng = np.random.default_rng(28)
+    for K, T, steps, ragged in ((4, 3, 5, False), (3, 2, 4, True)):
+        C = 2
+        init = rng.standard_normal((K - 1, C))
+        other = rng.standard_normal((K - 1, C))
+        xs = [rng.standard_normal((2, T, C)) for _ in range(steps)]
+        w = rng.standard_normal((C, K))
+        b = rng.standard_normal(C)
+        slots = np.array([0, -1], np.int32)
+        if ragged:
+            pairs = [(wd, a) for wd in range(T + 1) for a in range(wd + 1)]
+        else:
+            pairs = [(T, a) for a in range(T + 1)]
+        for seq in itertools.product(pairs, repeat=steps):
+            states = {0: init.copy(), 1: other.copy()}
+            stream = cv.ConvStream({0: init.copy()})
+            for j, (wd, a) in enumerate(seq):
+                lens = np.array([wd, 0], np.int32) if ragged else None
+                y = np.full((2, T, C), np.nan)
+                y[0, :wd] = cv.conv_verify(states[0], xs[j][0, :wd], w, b, cv.ACT_SILU)
+                y_def = stream.verify(slots, xs[j], w, b, cv.ACT_SILU, lens=lens)
+                assert np.array_equal(y[0, :wd], y_def[0, :wd])
+                acc = np.array([a, T], np.int32)
+                cv.conv_commit(states, slots, xs[j], acc, lens=lens)
+                stream.accept(slots, xs[j], acc, lens=lens)
+                assert np.array_equal(states[0], stream.state(0, K)), ('rolled state', seq, j)
+                assert np.array_equal(states[1], other)
+
+
 ALL_PINS = [pin_exact_rational, pin_exact_grouped_heads, pin_pure_decay, pin_identity_readout,
             pin_write_then_read, pin_grouped_write, pin_replay_equals_sequential,
             pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation,
             pin_ragged_replay_equals_sequential, pin_ragged_cursor_bruteforce, pin_query_scale,
-            pin_fold_policies]
+            pin_fold_policies, pin_conv_correlate, pin_conv_taps, pin_conv_rollback_bruteforce]

@@ -2,6 +2,7 @@
 import numpy as np
 import pytest
 
+import oracle.conv as cv
 import oracle.delta_rule as dr
 import oracle.replay as rp
 from tests import oracle_pins as pins
@@ -100,6 +101,32 @@ def _lazy_ignores_next_width(policy, m, next_T, L, masked_in):
                                                                                 L, masked_in)
 
 
+def _rolled_one_late(state, xw, a):
+    seq = np.concatenate([state, xw[:a + 1]], axis=0)
+    return seq[len(seq) - state.shape[0]:].copy()
+
+
+def _rolled_newest_first(state, xw, a):
+    seq = np.concatenate([state, xw[:a]], axis=0)
+    return seq[len(seq) - state.shape[0]:][::-1].copy()
+
+
+def _conv_taps_reversed(seq, t, w, b, act):
+    K = w.shape[1]
+    y = np.zeros(seq.shape[1])
+    for j in range(K):
+        y = y + w[:, K - 1 - j] * seq[t - K + 1 + j]
+    return cv.activate(y + (0 if b is None else b), act)
+
+
+def _conv_bias_after_act(seq, t, w, b, act):
+    K = w.shape[1]
+    y = np.zeros(seq.shape[1])
+    for j in range(K):
+        y = y + w[:, j] * seq[t - K + 1 + j]
+    return cv.activate(y, act) + (0 if b is None else b)
+
+
 MUTANTS = {
     'ragged window width ignored': [('window', _window_ignored)],
     'd sign flipped': [('token_update', _tu_sign)],
@@ -118,13 +145,17 @@ MUTANTS = {
     'force policy ignores its mask': [('policy_folds', _force_ignores_mask)],
     'force policy mask inverted': [('policy_folds', _force_mask_inverted)],
     'lazy policy ignores the next window width': [('policy_folds', _lazy_ignores_next_width)],
+    'conv state rolled one input late': [('rolled_state', _rolled_one_late)],
+    'conv state kept newest first': [('rolled_state', _rolled_newest_first)],
+    'conv taps reversed': [('conv_at', _conv_taps_reversed)],
+    'conv bias added after the activation': [('conv_at', _conv_bias_after_act)],
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_reject_mutant(name, monkeypatch):
     for attr, fn in MUTANTS[name]:
-        for mod in (dr, rp):
+        for mod in (dr, rp, cv):
             if hasattr(mod, attr):
                 monkeypatch.setattr(mod, attr, fn)
     caught = []
