@@ -657,6 +657,82 @@ def snapshot_baseline(name='c2', steps=30, warmup=10, layers=8):
             'ring_bytes_per_layer': cfg.B * cfg.L * b['record']}
 
 
+def conv_workload(name='conv_spec', steps=30, warmup=10, min_pool_bytes=1 << 30):
+    """The conv window of a GDN layer (rs_conv_verify, then rs_conv_commit with the step's
+    accept lengths) on Qwen3.5-shaped channels (2 x 16 x 128 q/k + 32 x 128 v), bf16
+    inputs, taps and state, fp32 outputs, width 4, SiLU.  Layer pools (state, inputs,
+    outputs) rotate past 1 GiB; one rollback launch covers every layer (layer-major
+    stacks).  Kernel times from one pair of HIP events around each step's verifies and one
+    around its rollback, divided by the layers.  Algorithmic bytes: verify
+    = per live row the K-1 state rows, the window inputs and outputs, plus the taps and
+    bias once; commit = per live row with accept > 0 its K-1 new state rows read and
+    written."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    cfg = W.CONV_CONFIGS[name]
+    rc = cfg.as_config()
+    dev = torch.device('cuda:0')
+    g = torch.Generator(device=dev).manual_seed(77)
+    a, o = 2, 4
+    per_layer = (cfg.num_slots * (cfg.K - 1) * cfg.C * a + cfg.B * cfg.T * cfg.C * (a + o))
+    layers = max(8, -(-min_pool_bytes // per_layer))
+    bf = torch.bfloat16
+    # layer-major stacks: one rollback launch covers every layer, as after the last layer
+    state = torch.randn(layers, cfg.num_slots, cfg.K - 1, cfg.C, generator=g, device=dev).to(bf)
+    xs = torch.randn(layers, cfg.B * cfg.T, cfg.C, generator=g, device=dev).to(bf)
+    ys = [torch.empty(cfg.B * cfg.T, cfg.C, device=dev) for _ in range(layers)]
+    w = (torch.randn(cfg.C, cfg.K, generator=g, device=dev) / 2).to(bf)
+    b = (0.1 * torch.randn(cfg.C, generator=g, device=dev)).to(bf)
+    slots_np = W.slot_map(rc)
+    slots = torch.from_numpy(slots_np.astype(np.int32)).to(dev)
+    live = [r for r in range(cfg.B) if slots_np[r] >= 0]
+    total = warmup + steps
+    accs_np = [W.accept_lengths(rc, j) for j in range(total)]
+    accs = [torch.from_numpy(x.astype(np.int32)).to(dev) for x in accs_np]
+    d = rs.ConvDims(cfg.B, cfg.T, cfg.C, cfg.K, cfg.num_slots, rs.BF16, rs.F32, rs.ACT_SILU)
+    verify = [rs.prepare_conv_verify(d, xs[l], w, b, state[l], slots, ys[l]) for l in range(layers)]
+    commit = [rs.prepare_conv_commit(d, state, xs, slots, accs[j], layers=layers)
+              for j in range(total)]
+    v_b = len(live) * ((cfg.K - 1) * cfg.C * a + cfg.T * cfg.C * (a + o) + 8) + cfg.C * (cfg.K + 1) * a
+    c_b = [sum(2 * (cfg.K - 1) * cfg.C * a + 8 for r in live if accs_np[j][r] > 0) for j in range(total)]
+    stream = torch.cuda.current_stream()
+    ev_v, ev_c = [], []
+
+    def step(j, timed):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed else None
+        if timed:
+            e[0].record(stream)
+        for l in range(layers):
+            verify[l](stream)
+        if timed:
+            e[1].record(stream)
+        commit[j](stream)
+        if timed:
+            e[2].record(stream)
+            ev_v.append((e[0], e[1]))
+            ev_c.append((e[1], e[2]))
+
+    for j in range(warmup):
+        step(j, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(warmup, total):
+        step(j, True)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    v_us = float(np.mean([x.elapsed_time(y) for x, y in ev_v])) * 1e3 / layers
+    c_us = float(np.mean([x.elapsed_time(y) for x, y in ev_c])) * 1e3 / layers
+    cb = float(np.mean(c_b[warmup:]))
+    return {'workload': name, 'batch': cfg.B, 'T': cfg.T, 'channels': cfg.C, 'width': cfg.K,
+            'layers': layers, 'ms_per_step': round(step_s * 1e3, 5),
+            'verify_us': round(v_us, 3), 'verify_bytes_per_launch': int(v_b),
+            'verify_gbs': round(v_b / v_us / 1e3, 1), 'verify_frac': _frac(v_b, v_us),
+            'commit_us': round(c_us, 3), 'commit_bytes_per_launch': int(cb),
+            'commit_gbs': round(cb / c_us / 1e3, 1), 'commit_frac': _frac(cb, c_us),
+            'tokens_per_s_per_layer': round(len(live) * cfg.T * layers / step_s, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -674,7 +750,7 @@ def main():
                     help='skip the history states and the other workloads')
     ap.add_argument('--only-workload', default='',
                     help='run one of the other workloads (c2, c3, c4, ragged_gdn, '
-                         'ragged_kda, snapshot_c2) alone and exit')
+                         'ragged_kda, snapshot_c2, conv_decode, conv_spec) alone and exit')
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -691,6 +767,8 @@ def main():
             copy_calibration()
         if args.only_workload.startswith('snapshot_'):
             print(json.dumps(snapshot_baseline(args.only_workload[len('snapshot_'):])), flush=True)
+        elif args.only_workload.startswith('conv_'):
+            print(json.dumps(conv_workload(args.only_workload)), flush=True)
         else:
             print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
         return
@@ -759,6 +837,9 @@ def main():
             print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
         extra['snapshot_baseline_c2'] = snapshot_baseline('c2')
         print(f'# snapshot baseline: {extra["snapshot_baseline_c2"]}', file=sys.stderr, flush=True)
+        for name in ('conv_decode', 'conv_spec'):
+            extra[name] = conv_workload(name)
+            print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
     if extra:
         line['extra'] = extra
     if cpu is not None:

@@ -274,6 +274,65 @@ rs_status rs_snapshot_commit(const rs_dims* dims, void* state, const void* snaps
                              const int32_t* slot_idx, const int32_t* accept_len,
                              hipStream_t stream);
 
+/*
+ * The short causal convolution a GDN layer applies to its mixed q/k/v channels before the
+ * recurrence, with its per-slot window state, and the rollback of that window at commit
+ * (LightLLM PR description: Conv/SSM state management with MTP accept and rollback;
+ * commit messages: page save and PD/DP copy "the accepted conv window" with the canonical
+ * SSM, a restored slot receives the canonical conv and SSM state; sglang PR commit 4: the
+ * GDN ring commit includes the conv rollback).  The pages do not give the convolution;
+ * this library takes the depthwise causal form
+ *     y_t[c] = act( sum_{j<K} weight[c][j] * x_{t-K+1+j}[c] + bias[c] ),
+ * tap K-1 on the current input, act = none or SiLU, where the inputs before the window
+ * come from the slot's conv state: its last K-1 committed inputs, oldest first.
+ *
+ * rs_conv_dims:  batch B; T the verify window (1..16; the widest window with cu_seqlens);
+ * channels C (a multiple of 8); width K (2, 3 or 4); num_slots; act_dtype of x, weight,
+ * bias and state; out_dtype of y (bf16: round to nearest even); activation.
+ */
+typedef enum { RS_ACT_NONE = 0, RS_ACT_SILU = 1 } rs_activation;
+
+typedef struct {
+    int32_t batch, T, channels, width, num_slots;
+    rs_dtype act_dtype, out_dtype;
+    rs_activation activation;
+} rs_conv_dims;
+
+/*
+ * rs_conv_verify -- the window's conv outputs; the conv state is read, never written.
+ *   cu_seqlens  NULL: row r's T inputs are tokens [r*T, r*T + T); else row r owns tokens
+ *               [cu_seqlens[r], cu_seqlens[r+1]) of total_tokens packed tokens (at most T;
+ *               clamped as for rs_gdn_verify_varlen), a width-0 window writes nothing
+ *   x           [tokens, C] act dtype (tokens = B*T, or total_tokens)
+ *   weight      [C, K] act dtype;  bias [C] act dtype or NULL
+ *   conv_state  [num_slots, K-1, C] act dtype, oldest input first
+ *   slot_idx    [B]; a negative slot is a null row: nothing is read or written
+ *   y           [tokens, C] out dtype; rows of null rows are not written
+ * Buffers are device memory, 16-byte aligned.  Enqueued on stream, no synchronisation.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE, RS_E_DTYPE, RS_E_VALUE (activation), RS_E_LAUNCH.
+ */
+rs_status rs_conv_verify(const rs_conv_dims* dims, const int32_t* cu_seqlens,
+                         int32_t total_tokens, const void* x, const void* weight,
+                         const void* bias, const void* conv_state, const int32_t* slot_idx,
+                         void* y, hipStream_t stream);
+
+/*
+ * rs_conv_commit -- the conv rollback after a step's verifies: for each live row with
+ * accept length a > 0 (clamped to [0, T_r]), the slot's state becomes inputs [a, a + K - 1)
+ * of state ++ window, i.e. the K-1 inputs ending at the last accepted draft; a = 0 leaves
+ * it.  cu_seqlens, total_tokens and x exactly as the step's rs_conv_verify calls received
+ * them; accept_len [B] int32.  A bit copy: no arithmetic.
+ *   layers      1..65535: one launch rolls back this many layers whose conv states
+ *               ([layers, num_slots, K-1, C]) and window inputs ([layers, tokens, C]) sit
+ *               back to back, layer-major (the rollback follows the last layer, as the
+ *               cursor advance does, so the layers' bytes share one launch's latency)
+ * Errors as rs_conv_verify; also RS_E_SHAPE for layers out of range.
+ */
+rs_status rs_conv_commit(const rs_conv_dims* dims, const int32_t* cu_seqlens,
+                         int32_t total_tokens, int32_t layers, void* conv_state,
+                         const void* x, const int32_t* slot_idx, const int32_t* accept_len,
+                         hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* rs_status_str(rs_status status);
 

@@ -22,9 +22,12 @@ __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'com
            'prepare_verify_varlen', 'prepare_cursor_advance_varlen',
            'materialize', 'verify_launch_info', 'stream_read', 'library_path', 'F32', 'BF16',
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
-           'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE', 'gdn_verify_noalloc']
+           'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE', 'gdn_verify_noalloc',
+           'ConvDims', 'conv_verify', 'conv_commit', 'prepare_conv_verify',
+           'prepare_conv_commit', 'ACT_NONE', 'ACT_SILU']
 
 F32, BF16 = 0, 1
+ACT_NONE, ACT_SILU = 0, 1
 FOLD_NONE, FOLD_EVERY_COMMIT, FOLD_LAZY, FOLD_FORCE = 0, 1, 2, 3
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -55,6 +58,17 @@ class Dims(ctypes.Structure):
 
     def __repr__(self):
         return 'Dims(' + ', '.join(f'{f}={getattr(self, f)}' for f, _ in self._fields_) + ')'
+
+
+class ConvDims(ctypes.Structure):
+    """rs_conv_dims: batch, T, channels, width, num_slots, act_dtype, out_dtype, activation."""
+    _fields_ = [('batch', ctypes.c_int32), ('T', ctypes.c_int32), ('channels', ctypes.c_int32),
+                ('width', ctypes.c_int32), ('num_slots', ctypes.c_int32),
+                ('act_dtype', ctypes.c_int), ('out_dtype', ctypes.c_int),
+                ('activation', ctypes.c_int)]
+
+    def __repr__(self):
+        return 'ConvDims(' + ', '.join(f'{f}={getattr(self, f)}' for f, _ in self._fields_) + ')'
 
 
 _LIB = None
@@ -96,6 +110,11 @@ def _lib():
         lib.rs_status_str.restype = ctypes.c_char_p
         lib.rs_verify_launch_info.argtypes = [dp, ctypes.c_int, _P, _P, _P]
         lib.rs_verify_launch_info.restype = ctypes.c_int
+        cdp = ctypes.POINTER(ConvDims)
+        lib.rs_conv_verify.argtypes = [cdp, _P, ctypes.c_int32] + [_P] * 6 + [_P]
+        lib.rs_conv_verify.restype = ctypes.c_int
+        lib.rs_conv_commit.argtypes = [cdp, _P, ctypes.c_int32, ctypes.c_int32] + [_P] * 4 + [_P]
+        lib.rs_conv_commit.restype = ctypes.c_int
         lib.rs_stream_read.argtypes = [_P, ctypes.c_uint64, _P, _P]
         lib.rs_stream_read.restype = ctypes.c_int
         _LIB = lib
@@ -306,6 +325,87 @@ def snapshot_commit(d: Dims, state, snapshots, slot_idx, accept_len, stream=None
             _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
     _check(_lib().rs_snapshot_commit(ctypes.byref(d), *args, _stream(stream)),
            'rs_snapshot_commit')
+
+
+def _conv_common(d: ConvDims, cu_seqlens, x):
+    at = _TORCH_DTYPE[d.act_dtype]
+    if cu_seqlens is None:
+        ntok = d.batch * d.T
+        cu = None
+    else:
+        if x is None or x.dim() < 1:
+            raise ValueError('x must be a [total_tokens, channels] tensor')
+        ntok = int(x.shape[0])
+        cu = _ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32)
+    return at, ntok, cu
+
+
+def conv_verify(d: ConvDims, x, weight, bias, conv_state, slot_idx, y, cu_seqlens=None,
+                stream=None):
+    """rs_conv_verify: the window's conv outputs y [tokens, C] (out dtype) from the window
+    inputs x [tokens, C], weight [C, K], bias [C] or None and the conv state
+    [num_slots, K-1, C]; cu_seqlens [B + 1] for ragged windows (tokens = x.shape[0])."""
+    at, ntok, cu = _conv_common(d, cu_seqlens, x)
+    C, K = d.channels, d.width
+    args = [_ptr(x, 'x', ntok * C, at), _ptr(weight, 'weight', C * K, at),
+            _ptr(bias, 'bias', C, at, optional=True),
+            _ptr(conv_state, 'conv_state', d.num_slots * (K - 1) * C, at),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(y, 'y', ntok * C, _TORCH_DTYPE[d.out_dtype])]
+    _check(_lib().rs_conv_verify(ctypes.byref(d), cu, ctypes.c_int32(ntok), *args,
+                                 _stream(stream)), 'rs_conv_verify')
+
+
+def conv_commit(d: ConvDims, conv_state, x, slot_idx, accept_len, cu_seqlens=None, layers=1,
+                stream=None):
+    """rs_conv_commit: roll each live row's conv state to the K-1 inputs ending at its
+    last accepted draft (x, cu_seqlens as the step's conv_verify calls received them).
+    layers > 1: conv_state [layers, num_slots, K-1, C] and x [layers, tokens, C], one
+    launch for all of them."""
+    at, ntok, cu = _conv_common(d, cu_seqlens, None if x is None or cu_seqlens is None
+                                else x.reshape(layers, -1, d.channels)[0])
+    C, K = d.channels, d.width
+    args = [_ptr(conv_state, 'conv_state', layers * d.num_slots * (K - 1) * C, at),
+            _ptr(x, 'x', layers * ntok * C, at), _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    _check(_lib().rs_conv_commit(ctypes.byref(d), cu, ctypes.c_int32(ntok), ctypes.c_int32(layers),
+                                 *args, _stream(stream)), 'rs_conv_commit')
+
+
+def prepare_conv_verify(d: ConvDims, x, weight, bias, conv_state, slot_idx, y, cu_seqlens=None):
+    """conv_verify with the tensors checked and marshalled once (for launch loops)."""
+    at, ntok, cu = _conv_common(d, cu_seqlens, x)
+    C, K = d.channels, d.width
+    args = [_ptr(x, 'x', ntok * C, at), _ptr(weight, 'weight', C * K, at),
+            _ptr(bias, 'bias', C, at, optional=True),
+            _ptr(conv_state, 'conv_state', d.num_slots * (K - 1) * C, at),
+            _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(y, 'y', ntok * C, _TORCH_DTYPE[d.out_dtype])]
+    fn, dref, nt = _lib().rs_conv_verify, ctypes.byref(d), ctypes.c_int32(ntok)
+
+    def call(stream=None):
+        st = fn(dref, cu, nt, *args, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_conv_verify')
+    call.tensors = (x, weight, bias, conv_state, slot_idx, y, cu_seqlens)
+    return call
+
+
+def prepare_conv_commit(d: ConvDims, conv_state, x, slot_idx, accept_len, layers=1):
+    """conv_commit (uniform windows) with the tensors checked and marshalled once."""
+    at = _TORCH_DTYPE[d.act_dtype]
+    C, K, ntok = d.channels, d.width, d.batch * d.T
+    args = [_ptr(conv_state, 'conv_state', layers * d.num_slots * (K - 1) * C, at),
+            _ptr(x, 'x', layers * ntok * C, at), _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+            _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
+    fn, dref = _lib().rs_conv_commit, ctypes.byref(d)
+
+    def call(stream=None):
+        st = fn(dref, None, ctypes.c_int32(ntok), ctypes.c_int32(layers), *args, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_conv_commit')
+    call.tensors = (conv_state, x, slot_idx, accept_len)
+    return call
 
 
 def verify_launch_info(d: Dims, kda: bool = False):

@@ -4,6 +4,7 @@
 
 #include "rs.h"
 #include "rs_internal.h"
+#include "rs_conv.h"
 #include "rs_snapshot.h"
 
 namespace {
@@ -180,9 +181,63 @@ rs_status fold_impl(const rs_dims* d, int is_kda, const void* state_in, void* st
   return e == hipSuccess ? RS_OK : RS_E_LAUNCH;
 }
 
+rs_status conv_check(const rs_conv_dims* d, const int32_t* cu_seqlens, int32_t ntok) {
+  if (!d) return RS_E_NULLPTR;
+  if (!dtype_ok(d->act_dtype) || !dtype_ok(d->out_dtype)) return RS_E_DTYPE;
+  if (d->batch < 0 || d->T < 1 || d->T > 16 || d->num_slots < 1) return RS_E_SHAPE;
+  if (d->channels < 8 || d->channels % 8 != 0) return RS_E_SHAPE;
+  if (d->width < 2 || d->width > 4) return RS_E_SHAPE;
+  if (cu_seqlens && ntok < 0) return RS_E_SHAPE;
+  if (d->activation != RS_ACT_NONE && d->activation != RS_ACT_SILU) return RS_E_VALUE;
+  return RS_OK;
+}
+
+rs::ConvArgs conv_args(const rs_conv_dims* d) {
+  rs::ConvArgs a{};
+  a.B = d->batch; a.T = d->T; a.C = d->channels; a.num_slots = d->num_slots; a.layers = 1;
+  a.out_bf16 = d->out_dtype == RS_BF16; a.silu = d->activation == RS_ACT_SILU;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
+
+rs_status rs_conv_verify(const rs_conv_dims* dims, const int32_t* cu_seqlens,
+                         int32_t total_tokens, const void* x, const void* weight,
+                         const void* bias, const void* conv_state, const int32_t* slot_idx,
+                         void* y, hipStream_t stream) {
+  const rs_status st = conv_check(dims, cu_seqlens, total_tokens);
+  if (st != RS_OK) return st;
+  if (dims->batch == 0) return RS_OK;
+  if (!x || !weight || !conv_state || !slot_idx || !y) return RS_E_NULLPTR;
+  rs::ConvArgs a = conv_args(dims);
+  a.x = x; a.weight = weight; a.bias = bias; a.state = conv_state; a.slot_idx = slot_idx;
+  a.y = y;
+  const rs::RowWindows w{cu_seqlens, total_tokens};
+  return rs::launch_conv_verify(dims->act_dtype == RS_BF16, dims->width, tmax_of(dims->T), a, w,
+                                stream) == hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
+rs_status rs_conv_commit(const rs_conv_dims* dims, const int32_t* cu_seqlens,
+                         int32_t total_tokens, int32_t layers, void* conv_state, const void* x,
+                         const int32_t* slot_idx, const int32_t* accept_len,
+                         hipStream_t stream) {
+  const rs_status st = conv_check(dims, cu_seqlens, total_tokens);
+  if (st != RS_OK) return st;
+  if (layers < 1 || layers > 65535) return RS_E_SHAPE;
+  if (dims->batch == 0) return RS_OK;
+  if (!conv_state || !x || !slot_idx || !accept_len) return RS_E_NULLPTR;
+  rs::ConvArgs a = conv_args(dims);
+  a.x = x; a.state_rw = conv_state; a.slot_idx = slot_idx; a.accept = accept_len;
+  a.layers = layers;
+  a.state_layer_stride = (size_t)dims->num_slots * (dims->width - 1) * dims->channels;
+  a.x_layer_stride = (size_t)(cu_seqlens ? total_tokens : dims->batch * dims->T) * dims->channels;
+  const rs::RowWindows w{cu_seqlens, total_tokens};
+  return rs::launch_conv_commit(dims->act_dtype == RS_BF16, dims->width, a, w, stream) ==
+                 hipSuccess ? RS_OK : RS_E_LAUNCH;
+}
+
 
 rs_status rs_gdn_verify(const rs_dims* dims, const void* q, const void* k, const void* v,
                         const void* beta, const void* gate, void* state, void* ring_k,

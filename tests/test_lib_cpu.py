@@ -153,3 +153,39 @@ def test_snapshot_validation():
     empty = _dims(batch=0, T=4)
     assert lib.rs_snapshot_verify(ctypes.byref(empty), 0, *([None] * 9), None) == 0
     assert lib.rs_snapshot_commit(ctypes.byref(empty), *([None] * 4), None) == 0
+
+
+def _cdims(**kw):
+    d = dict(batch=4, T=2, channels=64, width=4, num_slots=8, act_dtype=rs.BF16,
+             out_dtype=rs.F32, activation=rs.ACT_SILU)
+    d.update(kw)
+    return rs.ConvDims(*[d[f] for f, _ in rs.ConvDims._fields_])
+
+
+@pytest.mark.parametrize('kw,code', [
+    (dict(T=0), 2), (dict(T=17), 2), (dict(channels=12), 2), (dict(channels=0), 2),
+    (dict(width=1), 2), (dict(width=5), 2), (dict(num_slots=0), 2), (dict(batch=-1), 2),
+    (dict(act_dtype=5), 3), (dict(out_dtype=9), 3), (dict(activation=2), 6),
+])
+def test_conv_validation(kw, code):
+    """The conv window's entry points validate on the host before any launch."""
+    lib = rs._lib()
+    fake = ctypes.c_void_p(256)
+    d = _cdims(**kw)
+    assert lib.rs_conv_verify(ctypes.byref(d), None, 0, *([fake] * 6), None) == code
+    assert lib.rs_conv_commit(ctypes.byref(d), None, 0, 1, *([fake] * 4), None) == code
+
+
+def test_conv_nullptr_and_empty():
+    lib = rs._lib()
+    fake = ctypes.c_void_p(256)
+    d = _cdims()
+    assert lib.rs_conv_verify(ctypes.byref(d), None, 0, None, *([fake] * 5), None) == 1
+    assert lib.rs_conv_commit(ctypes.byref(d), None, 0, 1, fake, fake, fake, None, None) == 1
+    assert lib.rs_conv_commit(ctypes.byref(d), None, 0, 0, *([fake] * 4), None) == 2   # layers
+    assert lib.rs_conv_commit(ctypes.byref(d), None, 0, 65536, *([fake] * 4), None) == 2
+    assert lib.rs_conv_verify(ctypes.byref(d), fake, -1, *([fake] * 6), None) == 2
+    empty = _cdims(batch=0)
+    assert lib.rs_conv_verify(ctypes.byref(empty), None, 0, *([None] * 6), None) == 0
+    assert lib.rs_conv_commit(ctypes.byref(empty), None, 0, 1, *([None] * 4), None) == 0
+    assert lib.rs_conv_verify(None, None, 0, *([None] * 6), None) == 1

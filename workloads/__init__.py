@@ -311,3 +311,65 @@ def step_inputs(cfg: Config, step: int, layer: int = 0,
 def reduced(cfg: Config, **kw) -> Config:
     """A smaller copy of a config for exhaustive (all-row) parity at oracle-friendly sizes."""
     return cfg.with_(**kw)
+
+
+# ----------------------------------------------------------------------------- conv window
+# The short causal convolution before the recurrence: window inputs, taps, bias and the
+# initial per-slot window state, all drawn at random (nothing of the convolution itself).
+
+@dataclass(frozen=True)
+class ConvConfig:
+    name: str
+    B: int
+    null_rows: int
+    C: int               # channels (the mixed q/k/v channels of a GDN layer)
+    K: int               # convolution width
+    T: int               # verify window
+    accept: tuple
+    steps: int
+    act_dtype: str = 'bf16'
+    out_dtype: str = 'f32'
+    silu: bool = True
+    bias: bool = True
+    seed: int = 7
+    extra_slots: int = 16
+    ragged: tuple = ()
+
+    @property
+    def num_slots(self) -> int:
+        return self.B + self.extra_slots
+
+    def with_(self, **kw) -> "ConvConfig":
+        return replace(self, **kw)
+
+    def as_config(self) -> Config:
+        """The matching recurrent-layer config, for the slot map, accepts and windows."""
+        return Config(self.name, False, B=self.B, null_rows=self.null_rows, hk=1, hv=1, dk=16,
+                      dv=16, state_dtype='f32', act_dtype=self.act_dtype, L=max(self.T, 16),
+                      T=self.T, accept=self.accept, steps=self.steps, seed=self.seed,
+                      extra_slots=self.extra_slots, ragged=self.ragged)
+
+
+# Qwen3.5-shaped GDN layer: 16 key heads x 128 for q and for k, 32 value heads x 128 for v
+CONV_CONFIGS = {
+    'conv_decode': ConvConfig('conv_decode', B=64, null_rows=4, C=2 * 16 * 128 + 32 * 128, K=4,
+                              T=1, accept=('const', 1), steps=8),
+    'conv_spec': ConvConfig('conv_spec', B=128, null_rows=0, C=2 * 16 * 128 + 32 * 128, K=4,
+                            T=4, accept=('uniform', 0, 4), steps=8, seed=8),
+}
+
+
+def conv_params(cfg: ConvConfig):
+    """(weight [C, K], bias [C] or None, initial state [num_slots, K-1, C]) in the
+    activation dtype, as float64."""
+    rng = _rng(cfg.as_config(), 9)
+    w = to_dtype(rng.standard_normal((cfg.C, cfg.K)) / np.sqrt(cfg.K), cfg.act_dtype)
+    b = to_dtype(0.1 * rng.standard_normal(cfg.C), cfg.act_dtype) if cfg.bias else None
+    st = to_dtype(rng.standard_normal((cfg.num_slots, cfg.K - 1, cfg.C)), cfg.act_dtype)
+    return w, b, st
+
+
+def conv_inputs(cfg: ConvConfig, step: int) -> np.ndarray:
+    """Window inputs x [B, T, C] of a step, N(0, 1) in the activation dtype."""
+    rng = _rng(cfg.as_config(), 10, step)
+    return to_dtype(rng.standard_normal((cfg.B, cfg.T, cfg.C)), cfg.act_dtype)
