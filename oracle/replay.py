@@ -195,6 +195,31 @@ def materialize(layer: ReplayLayer, cursor, slots, rows=None):
     return out
 
 
+def prefill(layer: ReplayLayer, cursor, slots, inp, lens, rows=None):
+    """Prefill of each row's prompt (LightLLM commit messages: prefill writes the canonical
+    SSM directly and leaves the cursor at zero).  ``inp`` holds q, k [B, P, hk, dk], v
+    [B, P, hv, dv], beta, gate [B, P, hv] with row r's prompt in its first lens[r] tokens.
+    The state runs token by token from the slot's canonical S, which then holds the
+    state after the last prompt token; the cursor becomes 0.  A slot's ring records are
+    not read: the caller folds any pending ones first (a forced commit), so S is the
+    committed state.  Returns out [B, P, hv, dv], NaN where no token was processed."""
+    B, P = inp.v.shape[:2]
+    out = np.full(inp.v.shape, np.nan)
+    for r in _rows(slots, rows):
+        s = int(slots[r])
+        if s not in layer.S:
+            continue
+        H = layer.S[s]
+        ks = expand_heads(inp.k[r], layer.G)
+        qs = expand_heads(inp.q[r], layer.G)
+        for t in range(int(lens[r])):
+            H, _ = token_update(H, ks[t], inp.v[r, t], inp.beta[r, t], inp.gate[r, t], layer.kda)
+            out[r, t] = readout(H, qs[t], layer.scale)
+        layer.S[s] = H
+        cursor[s] = 0
+    return out
+
+
 class TokenStream:
     """The definition: per slot, the committed state is the gated delta rule run over the
     accepted tokens in order; a verify runs the T draft tokens on from it."""

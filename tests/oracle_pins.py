@@ -649,8 +649,64 @@ def pin_conv_rollback_bruteforce():
                 assert np.array_equal(states[1], other)
 
 
+def pin_prefill_then_replay():
+    """Prefill hands over to the replay state machine: prompts of ragged lengths (0
+    included) through prefill, then verify steps with history, fused and commit folds,
+    equal the token-stream definition that takes each prompt as accepted tokens, at every
+    output and committed state (1e-12); prefill leaves every live cursor at 0 and a null
+    row's slot untouched; a prompt split in two prefill calls equals one call."""
+    rng = np.random.default_rng(29)
+    for kda in (False, True):
+        hk, hv, dk, dv, B, P, T, L, steps = 2, 4, 5, 4, 4, 9, 3, 7, 8
+        nslots = B + 2
+        S0 = rng.standard_normal((nslots, hv, dk, dv)) * 0.3
+        slots = np.array([2, -1, 5, 0], np.int32)
+        lens = np.array([9, 4, 0, 6], np.int32)
+        prompt = _inputs(B, P, hk, hv, dk, dv, kda, rng)
+        layer = _layer(S0, L, hk, hv, dk, dv, kda)
+        ts = rp.TokenStream({s: S0[s].copy() for s in range(nslots)}, kda, hv // hk)
+        cursor = np.full(nslots, 3, np.int32)          # stale counts: prefill clears them
+        out = rp.prefill(layer, cursor, slots, prompt, lens)
+        o_def, _ = ts.verify(slots, prompt, lens=lens)
+        ts.accept(slots, lens)
+        live = slots >= 0
+        assert np.array_equal(np.isfinite(out), np.isfinite(o_def))
+        fin = np.isfinite(o_def)
+        assert _rel(out[fin], o_def[fin]) < 1e-12, ('prefill outputs', kda)
+        assert np.all(cursor[slots[live]] == 0) and cursor[1] == 3 and cursor[4] == 3
+        assert np.array_equal(layer.S[4], S0[4]) and np.array_equal(layer.S[5], S0[5])
+        # split prompts: the first a tokens, then the rest, through two prefill calls
+        l2 = _layer(S0, L, hk, hv, dk, dv, kda)
+        c2 = np.zeros(nslots, np.int32)
+        first = np.minimum(lens, 3)
+        rp.prefill(l2, c2, slots, prompt, first)
+        rest = SimpleNamespace(**{f: np.concatenate([getattr(prompt, f)[:, 3:],
+                                                     getattr(prompt, f)[:, :3]], axis=1)
+                                  for f in ('q', 'k', 'v', 'beta', 'gate')})
+        rp.prefill(l2, c2, slots, rest, lens - first)
+        for s in (2, 5, 0):
+            assert _rel(l2.S[s], layer.S[s]) < 1e-12, ('split prefill', kda)
+        fl = np.zeros(nslots, np.int32)
+        for j in range(steps):
+            inp = _inputs(B, T, hk, hv, dk, dv, kda, rng)
+            acc = rng.integers(0, T + 1, size=B).astype(np.int32)
+            o_rep, _ = rp.verify(layer, cursor, slots, inp)
+            o2, _ = ts.verify(slots, inp)
+            f = np.isfinite(o2)
+            assert _rel(o_rep[f], o2[f]) < 1e-12, ('replay after prefill', kda, j)
+            pol = rp.FOLD_FORCE if j % 3 == 2 else rp.FOLD_NONE
+            rp.cursor_advance(cursor, fl, slots, acc, T, L, pol)
+            rp.commit_fold(layer, fl, slots)
+            ts.accept(slots, acc)
+            for r in range(B):
+                s_ = int(slots[r])
+                if s_ >= 0:
+                    assert _rel(layer.committed_state(s_, int(cursor[s_])), ts.H[s_]) < 1e-12
+
+
 ALL_PINS = [pin_exact_rational, pin_exact_grouped_heads, pin_pure_decay, pin_identity_readout,
             pin_write_then_read, pin_grouped_write, pin_replay_equals_sequential,
             pin_fold_invariance, pin_cursor_bruteforce, pin_c0_fold_count, pin_nan_isolation,
             pin_ragged_replay_equals_sequential, pin_ragged_cursor_bruteforce, pin_query_scale,
-            pin_fold_policies, pin_conv_correlate, pin_conv_taps, pin_conv_rollback_bruteforce]
+            pin_fold_policies, pin_conv_correlate, pin_conv_taps, pin_conv_rollback_bruteforce,
+            pin_prefill_then_replay]

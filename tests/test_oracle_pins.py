@@ -127,6 +127,27 @@ def _conv_bias_after_act(seq, t, w, b, act):
     return cv.activate(y, act) + (0 if b is None else b)
 
 
+_prefill = rp.prefill
+
+
+def _prefill_keeps_cursor(layer, cursor, slots, inp, lens, rows=None):
+    saved = cursor.copy()
+    out = _prefill(layer, cursor, slots, inp, lens, rows)
+    cursor[:] = saved
+    return out
+
+
+def _prefill_from_zero(layer, cursor, slots, inp, lens, rows=None):
+    for s in slots:
+        if s >= 0 and int(s) in layer.S:
+            layer.S[int(s)] = np.zeros_like(layer.S[int(s)])
+    return _prefill(layer, cursor, slots, inp, lens, rows)
+
+
+def _prefill_drops_last(layer, cursor, slots, inp, lens, rows=None):
+    return _prefill(layer, cursor, slots, inp, np.maximum(np.asarray(lens) - 1, 0), rows)
+
+
 MUTANTS = {
     'ragged window width ignored': [('window', _window_ignored)],
     'd sign flipped': [('token_update', _tu_sign)],
@@ -149,6 +170,9 @@ MUTANTS = {
     'conv state kept newest first': [('rolled_state', _rolled_newest_first)],
     'conv taps reversed': [('conv_at', _conv_taps_reversed)],
     'conv bias added after the activation': [('conv_at', _conv_bias_after_act)],
+    'prefill keeps the stale cursor': [('prefill', _prefill_keeps_cursor)],
+    'prefill starts from a zero state': [('prefill', _prefill_from_zero)],
+    'prefill drops the last prompt token': [('prefill', _prefill_drops_last)],
 }
 
 
