@@ -733,6 +733,70 @@ def conv_workload(name='conv_spec', steps=30, warmup=10, min_pool_bytes=1 << 30)
             'tokens_per_s_per_layer': round(len(live) * cfg.T * layers / step_s, 1)}
 
 
+def prefill_workload(B=16, P=512, steps=10, warmup=3):
+    """Chunked prefill (rs_gdn_prefill) of a Qwen3.5-shaped GDN layer: B requests with
+    P-token prompts each, 16 key / 32 value heads, dk = dv = 128, fp32 state, bf16 inputs.
+    Layer pools rotate (8, each with its own state and inputs, past 1 GiB).  Time from one
+    pair of HIP events around each step's launches, divided by the layers.  Algorithmic
+    bytes per launch: per row the state read and written once, and per token its q, k, v,
+    beta, gate (bf16) and output (fp32); flops: per token and value head 4 dk dv for the
+    readout of q and k, 2 dk dv for the state update, and the chunk's scores and solve."""
+    import torch
+    import linear_attention_recurrent_rs_amd as rs
+    import workloads as W
+    cfg = W.CONFIGS['c1'].with_(B=B, null_rows=0, cursor_init='zero')
+    dev = torch.device('cuda:0')
+    g = torch.Generator(device=dev).manual_seed(99)
+    layers = 8
+    bf = torch.bfloat16
+    ntok = B * P
+
+    def unit(*shape):
+        x = torch.randn(*shape, generator=g, device=dev)
+        return x / x.norm(dim=-1, keepdim=True)
+    S = [(torch.randn(cfg.num_slots, cfg.hv, cfg.dk, cfg.dv, generator=g, device=dev) * 0.05)
+         for _ in range(layers)]
+    ins = [(unit(ntok, cfg.hk, cfg.dk).to(bf), unit(ntok, cfg.hk, cfg.dk).to(bf),
+            torch.randn(ntok, cfg.hv, cfg.dv, generator=g, device=dev).to(bf),
+            torch.rand(ntok, cfg.hv, generator=g, device=dev).to(bf),
+            torch.exp(-torch.nn.functional.softplus(
+                torch.randn(ntok, cfg.hv, generator=g, device=dev))).to(bf))
+           for _ in range(layers)]
+    out = torch.empty(ntok, cfg.hv, cfg.dv, device=dev)
+    cursor = torch.zeros(cfg.num_slots, dtype=torch.int32, device=dev)
+    slots_np = W.slot_map(cfg)
+    slots = torch.from_numpy(slots_np.astype(np.int32)).to(dev)
+    cu = torch.arange(0, ntok + 1, P, dtype=torch.int32, device=dev)
+    d = rs.Dims(cfg.B, 1, cfg.hk, cfg.hv, cfg.dk, cfg.dv, cfg.L, cfg.num_slots, rs.BF16, rs.F32)
+    calls = [rs.prepare_gdn_prefill(d, cu, *ins[l], S[l], cursor, slots, out) for l in range(layers)]
+    stream = torch.cuda.current_stream()
+    for j in range(warmup):
+        for l in range(layers):
+            calls[l](stream)
+    torch.cuda.synchronize()
+    ev = []
+    t0 = time.perf_counter()
+    for j in range(steps):
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        e[0].record(stream)
+        for l in range(layers):
+            calls[l](stream)
+        e[1].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    us = float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) * 1e3 / layers
+    sbytes = cfg.hv * cfg.dk * cfg.dv * 4
+    tok_bytes = (2 * cfg.hk * cfg.dk + cfg.hv * cfg.dv + 2 * cfg.hv) * 2 + cfg.hv * cfg.dv * 4
+    byts = B * (2 * sbytes + 8) + ntok * tok_bytes
+    flops = ntok * cfg.hv * (6 * cfg.dk * cfg.dv + 4 * 16 * (cfg.dk + cfg.dv))
+    return {'workload': 'gdn_prefill', 'batch': B, 'prompt': P, 'chunk': 16, 'layers': layers,
+            'ms_per_step': round(step_s * 1e3, 4), 'kernel_us': round(us, 3),
+            'bytes_per_launch': int(byts), 'achieved_gbs': round(byts / us / 1e3, 1),
+            'frac_hbm': _frac(byts, us), 'tflops': round(flops / us / 1e6, 2),
+            'prefill_tokens_per_s_per_layer': round(ntok / (us * 1e-6), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -750,7 +814,7 @@ def main():
                     help='skip the history states and the other workloads')
     ap.add_argument('--only-workload', default='',
                     help='run one of the other workloads (c2, c3, c4, ragged_gdn, '
-                         'ragged_kda, snapshot_c2, conv_decode, conv_spec) alone and exit')
+                         'ragged_kda, snapshot_c2, conv_decode, conv_spec, prefill) alone and exit')
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -769,6 +833,8 @@ def main():
             print(json.dumps(snapshot_baseline(args.only_workload[len('snapshot_'):])), flush=True)
         elif args.only_workload.startswith('conv_'):
             print(json.dumps(conv_workload(args.only_workload)), flush=True)
+        elif args.only_workload == 'prefill':
+            print(json.dumps(prefill_workload()), flush=True)
         else:
             print(json.dumps(run_workload(args.only_workload, tile_v=args.tile_v)), flush=True)
         return
@@ -840,6 +906,8 @@ def main():
         for name in ('conv_decode', 'conv_spec'):
             extra[name] = conv_workload(name)
             print(f'# {name}: {extra[name]}', file=sys.stderr, flush=True)
+        extra['prefill_b16_p512'] = prefill_workload()
+        print(f'# prefill: {extra["prefill_b16_p512"]}', file=sys.stderr, flush=True)
     if extra:
         line['extra'] = extra
     if cpu is not None:

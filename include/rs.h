@@ -275,6 +275,29 @@ rs_status rs_snapshot_commit(const rs_dims* dims, void* state, const void* snaps
                              hipStream_t stream);
 
 /*
+ * rs_gdn_prefill -- chunked prefill of one GDN layer (LightLLM commit messages: prefill
+ * writes the canonical SSM directly and leaves the cursor at zero).  Row r's prompt, the
+ * packed tokens [cu_seqlens[r], cu_seqlens[r+1]) (any length, 0 allowed; clamped to
+ * [0, total_tokens]), runs from the slot's canonical state S through the gated delta rule;
+ * S is overwritten with the state after the last prompt token and cursor[slot] set to 0.
+ * The ring is not read: a slot with pending records must have them folded first (a FORCE
+ * rs_cursor_advance and rs_commit_fold), so that S is its committed state; a new request's
+ * S is zeroed by the caller; a long prompt may be split over calls.
+ *   q, k   [total_tokens, hk, 128] bf16;  v [total_tokens, hv, dv] bf16
+ *   beta, gate [total_tokens, hv] bf16;   out [total_tokens, hv, dv] fp32 (scale S^T q)
+ *   state  [num_slots, hv, 128, dv] state dtype (bf16: one rounding at the end)
+ *   cursor [num_slots] int32 (written: 0 for live rows); slot_idx [B] (null rows skipped)
+ * Covers dk = 128, bf16 inputs and dv a multiple of 64; dims->T, ring_cap and tile_v are
+ * not used.  The state stays on chip across the prompt, in chunks of 16 tokens.
+ * Errors: RS_E_NULLPTR, RS_E_SHAPE (other shapes, total_tokens < 0), RS_E_DTYPE,
+ * RS_E_VALUE (scale), RS_E_LAUNCH.
+ */
+rs_status rs_gdn_prefill(const rs_dims* dims, const int32_t* cu_seqlens, int32_t total_tokens,
+                         const void* q, const void* k, const void* v, const void* beta,
+                         const void* gate, void* state, int32_t* cursor,
+                         const int32_t* slot_idx, float* out, hipStream_t stream);
+
+/*
  * The short causal convolution a GDN layer applies to its mixed q/k/v channels before the
  * recurrence, with its per-slot window state, and the rollback of that window at commit
  * (LightLLM PR description: Conv/SSM state management with MTP accept and rollback;

@@ -24,7 +24,7 @@ __all__ = ['Dims', 'RSError', 'gdn_verify', 'kda_verify', 'cursor_advance', 'com
            'prepare_verify', 'prepare_cursor_advance', 'prepare_commit_fold',
            'FOLD_NONE', 'FOLD_EVERY_COMMIT', 'FOLD_LAZY', 'FOLD_FORCE', 'gdn_verify_noalloc',
            'ConvDims', 'conv_verify', 'conv_commit', 'prepare_conv_verify',
-           'prepare_conv_commit', 'ACT_NONE', 'ACT_SILU']
+           'prepare_conv_commit', 'ACT_NONE', 'ACT_SILU', 'gdn_prefill', 'prepare_gdn_prefill']
 
 F32, BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
@@ -110,6 +110,8 @@ def _lib():
         lib.rs_status_str.restype = ctypes.c_char_p
         lib.rs_verify_launch_info.argtypes = [dp, ctypes.c_int, _P, _P, _P]
         lib.rs_verify_launch_info.restype = ctypes.c_int
+        lib.rs_gdn_prefill.argtypes = [dp, _P, ctypes.c_int32] + [_P] * 9 + [_P]
+        lib.rs_gdn_prefill.restype = ctypes.c_int
         cdp = ctypes.POINTER(ConvDims)
         lib.rs_conv_verify.argtypes = [cdp, _P, ctypes.c_int32] + [_P] * 6 + [_P]
         lib.rs_conv_verify.restype = ctypes.c_int
@@ -325,6 +327,42 @@ def snapshot_commit(d: Dims, state, snapshots, slot_idx, accept_len, stream=None
             _ptr(accept_len, 'accept_len', d.batch, torch.int32)]
     _check(_lib().rs_snapshot_commit(ctypes.byref(d), *args, _stream(stream)),
            'rs_snapshot_commit')
+
+
+def _prefill_ptrs(d: Dims, cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out):
+    at, st = _TORCH_DTYPE[d.act_dtype], _TORCH_DTYPE[d.state_dtype]
+    ntok = _ntok(q)
+    return ntok, [_ptr(cu_seqlens, 'cu_seqlens', d.batch + 1, torch.int32),
+                  ctypes.c_int32(ntok),
+                  _ptr(q, 'q', ntok * d.hk * d.dk, at), _ptr(k, 'k', ntok * d.hk * d.dk, at),
+                  _ptr(v, 'v', ntok * d.hv * d.dv, at), _ptr(beta, 'beta', ntok * d.hv, at),
+                  _ptr(gate, 'gate', ntok * d.hv, at),
+                  _ptr(state, 'state', d.num_slots * d.hv * d.dk * d.dv, st),
+                  _ptr(cursor, 'cursor', d.num_slots, torch.int32),
+                  _ptr(slot_idx, 'slot_idx', d.batch, torch.int32),
+                  _ptr(out, 'out', ntok * d.hv * d.dv, torch.float32)]
+
+
+def gdn_prefill(d: Dims, cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out,
+                stream=None):
+    """rs_gdn_prefill: row r's prompt is packed tokens [cu_seqlens[r], cu_seqlens[r+1]) of
+    q [tokens, hk, 128] (tokens = q.shape[0]); S of each live slot becomes the state after
+    its prompt, its cursor 0; out [tokens, hv, dv] fp32."""
+    _, args = _prefill_ptrs(d, cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out)
+    _check(_lib().rs_gdn_prefill(ctypes.byref(d), *args, _stream(stream)), 'rs_gdn_prefill')
+
+
+def prepare_gdn_prefill(d: Dims, cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out):
+    """gdn_prefill with the tensors checked and marshalled once (for launch loops)."""
+    _, args = _prefill_ptrs(d, cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out)
+    fn, dref = _lib().rs_gdn_prefill, ctypes.byref(d)
+
+    def call(stream=None):
+        st = fn(dref, *args, _stream(stream))
+        if st:
+            raise RSError(st, 'rs_gdn_prefill')
+    call.tensors = (cu_seqlens, q, k, v, beta, gate, state, cursor, slot_idx, out)
+    return call
 
 
 def _conv_common(d: ConvDims, cu_seqlens, x):

@@ -25,7 +25,7 @@ COMMON = ['-O3', '-fPIC', '-std=c++17', f'--offload-arch={ARCH}', '-mcode-object
           '-I', os.path.join(ROOT, 'include'), '-I', CSRC, '-Wall', '-Wno-unused-function']
 
 SOURCES = ['rs_kernels.hip', 'rs_verify_fast.hip', 'rs_fold_fast.hip', 'rs_snapshot.hip',
-           'rs_probe.hip', 'rs_noalloc.hip', 'rs_conv.hip', 'rs_api.cpp']
+           'rs_probe.hip', 'rs_noalloc.hip', 'rs_conv.hip', 'rs_prefill.hip', 'rs_api.cpp']
 
 
 def _compile(src: str) -> str:

@@ -5,6 +5,7 @@
 #include "rs.h"
 #include "rs_internal.h"
 #include "rs_conv.h"
+#include "rs_prefill.h"
 #include "rs_snapshot.h"
 
 namespace {
@@ -202,6 +203,31 @@ rs::ConvArgs conv_args(const rs_conv_dims* d) {
 }  // namespace
 
 extern "C" {
+
+rs_status rs_gdn_prefill(const rs_dims* dims, const int32_t* cu_seqlens, int32_t total_tokens,
+                         const void* q, const void* k, const void* v, const void* beta,
+                         const void* gate, void* state, int32_t* cursor,
+                         const int32_t* slot_idx, float* out, hipStream_t stream) {
+  if (!dims) return RS_E_NULLPTR;
+  const rs_dims* d = dims;
+  if (!dtype_ok(d->act_dtype) || !dtype_ok(d->state_dtype)) return RS_E_DTYPE;
+  if (d->act_dtype != RS_BF16) return RS_E_DTYPE;
+  if (d->batch < 0 || d->hk < 1 || d->hv < 1 || d->hv % d->hk != 0 || d->num_slots < 1)
+    return RS_E_SHAPE;
+  if (d->dk != 128 || d->dv < 64 || d->dv % 64 != 0 || total_tokens < 0) return RS_E_SHAPE;
+  if (!scale_ok(d)) return RS_E_VALUE;
+  if (d->batch == 0) return RS_OK;
+  if (!cu_seqlens || !q || !k || !v || !beta || !gate || !state || !cursor || !slot_idx || !out)
+    return RS_E_NULLPTR;
+  rs::PrefillArgs a{};
+  a.B = d->batch; a.hk = d->hk; a.hv = d->hv; a.dv = d->dv; a.G = d->hv / d->hk;
+  a.NV = d->dv / 64; a.nblocks = d->batch * d->hv * a.NV; a.num_slots = d->num_slots;
+  a.ntok = total_tokens; a.scale = d->scale; a.cu_seqlens = cu_seqlens;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gate = gate; a.state = state; a.cursor = cursor;
+  a.slot_idx = slot_idx; a.out = out;
+  return rs::launch_prefill(d->state_dtype == RS_BF16, a, stream) == hipSuccess ? RS_OK
+                                                                               : RS_E_LAUNCH;
+}
 
 rs_status rs_conv_verify(const rs_conv_dims* dims, const int32_t* cu_seqlens,
                          int32_t total_tokens, const void* x, const void* weight,

@@ -163,6 +163,45 @@ __device__ __forceinline__ f4 mfma_bf16_16x16x16(s4 a, s4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ bf16 splits of fp32 values
+// (operands of bf16 MFMAs standing in for fp32 products)
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+
+// Four fp32 values (K entries 0..3 of an MFMA operand) split into bf16 parts, x = hi + lo
+// + e with |e| <= 2^-16 |x|: hi keeps the upper 16 bits (truncation), lo is the exact
+// remainder rounded to nearest even (one v_cvt_pk_bf16_f32 per pair).
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, s4& hi, s4& lo) {
+  const uint32_t w0 = __float_as_uint(x0), w1 = __float_as_uint(x1);
+  const uint32_t w2 = __float_as_uint(x2), w3 = __float_as_uint(x3);
+  hi = __builtin_bit_cast(s4, u2{(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)});
+  const f2 r01 = {x0 - __uint_as_float(w0 & 0xffff0000u), x1 - __uint_as_float(w1 & 0xffff0000u)};
+  const f2 r23 = {x2 - __uint_as_float(w2 & 0xffff0000u), x3 - __uint_as_float(w3 & 0xffff0000u)};
+  lo = __builtin_bit_cast(s4, u2{__builtin_bit_cast(uint32_t, __builtin_convertvector(r01, b2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(r23, b2))});
+}
+
+// Four fp32 values split into three bf16 parts, x = hi + mid + lo + e with
+// |e| <= 2^-24 |x|: hi and mid keep the upper 16 bits of x and of the exact remainder,
+// lo is the final remainder rounded to nearest even.
+__device__ __forceinline__ void split4x3(const float (&x)[4], s4& hi, s4& mid, s4& lo) {
+  uint32_t h[4], m[4];
+  f2 r[2];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t w = __float_as_uint(x[e]);
+    h[e] = w & 0xffff0000u;
+    const float r1 = x[e] - __uint_as_float(h[e]);
+    m[e] = __float_as_uint(r1) & 0xffff0000u;
+    r[e >> 1][e & 1] = r1 - __uint_as_float(m[e]);
+  }
+  hi = __builtin_bit_cast(s4, u2{(h[0] >> 16) | h[1], (h[2] >> 16) | h[3]});
+  mid = __builtin_bit_cast(s4, u2{(m[0] >> 16) | m[1], (m[2] >> 16) | m[3]});
+  lo = __builtin_bit_cast(s4, u2{__builtin_bit_cast(uint32_t, __builtin_convertvector(r[0], b2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(r[1], b2))});
+}
+
 // Direct HBM -> LDS copy of 16 bytes per lane: lane l writes lds_wave_base + 16*l.
 __device__ __forceinline__ void load_lds_16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base,

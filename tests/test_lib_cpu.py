@@ -189,3 +189,22 @@ def test_conv_nullptr_and_empty():
     assert lib.rs_conv_verify(ctypes.byref(empty), None, 0, *([None] * 6), None) == 0
     assert lib.rs_conv_commit(ctypes.byref(empty), None, 0, 1, *([None] * 4), None) == 0
     assert lib.rs_conv_verify(None, None, 0, *([None] * 6), None) == 1
+
+
+def test_prefill_validation():
+    """The prefill entry point validates on the host before any launch: it covers dk = 128
+    with bf16 inputs and dv a multiple of 64; it needs cu_seqlens and a valid scale."""
+    lib = rs._lib()
+    fake = ctypes.c_void_p(256)
+    f = lib.rs_gdn_prefill
+    ok = _dims(T=1)
+    assert f(ctypes.byref(ok), None, 8, *([fake] * 9), None) == 1          # cu_seqlens
+    assert f(ctypes.byref(ok), fake, 8, fake, None, *([fake] * 7), None) == 1
+    assert f(ctypes.byref(ok), fake, -1, *([fake] * 9), None) == 2
+    assert f(ctypes.byref(_dims(dk=64)), fake, 8, *([fake] * 9), None) == 2
+    assert f(ctypes.byref(_dims(dv=96)), fake, 8, *([fake] * 9), None) == 2
+    assert f(ctypes.byref(_dims(hv=3)), fake, 8, *([fake] * 9), None) == 2
+    assert f(ctypes.byref(_dims(act_dtype=rs.F32)), fake, 8, *([fake] * 9), None) == 3
+    assert f(ctypes.byref(_dims(scale=0.0)), fake, 8, *([fake] * 9), None) == 6
+    assert f(ctypes.byref(_dims(batch=0)), None, 0, *([None] * 9), None) == 0
+    assert f(None, fake, 8, *([fake] * 9), None) == 1
