@@ -682,6 +682,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
     }
   }
 
+  constexpr bool SPREAD = TMAX >= 8;
   // 8. tile part of the readout, S^T xr_m over this thread's rows; each wave's partial
   // goes to LDS, and the thread of column c gathers P_m = sum of the 4 partials (+ the
   // history part) into registers.
@@ -722,15 +723,15 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     lds_barrier();
-    if (tid < BV) {
+    if (SPREAD || tid < BV) {
       const float scale = fold ? 1.f : Gam;
 #pragma unroll
       for (int m = 0; m < NV2; ++m) {
         if (m < nvec) {
-          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
-                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
+          float p = (red[m * BV + tid % BV] + red[(NPd + m) * BV + tid % BV]) +
+                    (red[(2 * NPd + m) * BV + tid % BV] + red[(3 * NPd + m) * BV + tid % BV]);
           p *= scale * Gp[m >> 1];
-          if (hrows > 0) p += hist[m * BV + tid];
+          if (hrows > 0) p += hist[m * BV + tid % BV];
           Pv[m] = p;
         }
       }
@@ -772,15 +773,15 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     lds_barrier();
-    if (tid < BV) {
+    if (SPREAD || tid < BV) {
       const float scale = fold ? 1.f : Gam;
 #pragma unroll
       for (int m = 0; m < NV2; ++m) {
         if (m < nvec) {
-          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
-                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
+          float p = (red[m * BV + tid % BV] + red[(NPd + m) * BV + tid % BV]) +
+                    (red[(2 * NPd + m) * BV + tid % BV] + red[(3 * NPd + m) * BV + tid % BV]);
           p *= scale * Gp[m >> 1];
-          if (hrows > 0) p += hist[m * BV + tid];
+          if (hrows > 0) p += hist[m * BV + tid % BV];
           Pv[m] = p;
         }
       }
@@ -822,13 +823,13 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     lds_barrier();
-    if (tid < BV) {
+    if (SPREAD || tid < BV) {
 #pragma unroll
       for (int m = 0; m < NV2; ++m) {
         if (m < nvec) {
-          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
-                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
-          if (hrows > 0) p += hist[m * BV + tid];
+          float p = (red[m * BV + tid % BV] + red[(NPd + m) * BV + tid % BV]) +
+                    (red[(2 * NPd + m) * BV + tid % BV] + red[(3 * NPd + m) * BV + tid % BV]);
+          if (hrows > 0) p += hist[m * BV + tid % BV];
           Pv[m] = p;
         }
       }
@@ -867,14 +868,14 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     lds_barrier();
-    if (tid < BV) {
+    if (SPREAD || tid < BV) {
       const int NPd = lay.nvec_pad;
 #pragma unroll
       for (int m = 0; m < NV2; ++m) {
         if (m < nvec) {
-          float p = (red[m * BV + tid] + red[(NPd + m) * BV + tid]) +
-                    (red[(2 * NPd + m) * BV + tid] + red[(3 * NPd + m) * BV + tid]);
-          if (hrows > 0) p += hist[m * BV + tid];
+          float p = (red[m * BV + tid % BV] + red[(NPd + m) * BV + tid % BV]) +
+                    (red[(2 * NPd + m) * BV + tid % BV] + red[(3 * NPd + m) * BV + tid % BV]);
+          if (hrows > 0) p += hist[m * BV + tid % BV];
           Pv[m] = p;
         }
       }
@@ -945,22 +946,26 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         for (int mm = 0; mm < VPP; ++mm) store4(red + (wave * VPP + mm) * BV + 4 * cc, acc[mm]);
       }
       lds_barrier();
-      if (tid < BV) {
+      if (SPREAD || tid < BV) {
 #pragma unroll
         for (int mm = 0; mm < VPP; ++mm) {
           const int m = m0 + mm;
           if (m < nvec) {
-            Pv[m] = (red[mm * BV + tid] + red[(VPP + mm) * BV + tid]) +
-                    (red[(2 * VPP + mm) * BV + tid] + red[(3 * VPP + mm) * BV + tid]);
+            Pv[m] = (red[mm * BV + tid % BV] + red[(VPP + mm) * BV + tid % BV]) +
+                    (red[(2 * VPP + mm) * BV + tid % BV] + red[(3 * VPP + mm) * BV + tid % BV]);
           }
         }
       }
     }
   }
 
-  // 9. per column: forward substitution over the window, outputs, ring deltas
-  if (tid < BV) {
-    const int c = tid, col = col0 + c;
+  // 9. per column: forward substitution over the window, outputs, ring deltas.  Windows of
+  // 8 and more: every thread solves its column (tid % BV), and the kThreads / BV threads of
+  // a column share its 2T stores, which would otherwise queue behind one another in one
+  // wave.
+  if (SPREAD || tid < BV) {
+    constexpr int NQ = SPREAD ? kThreads / BV : 1;
+    const int c = tid % BV, col = col0 + c, grp = tid / BV;
     float d[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -977,14 +982,19 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         float o = Pv[2 * t];
 #pragma unroll
         for (int u = 0; u <= t; ++u) o = fmaf(Qm[t * TMAX + u], d[u], o);
-        a.out[((tok0 + t) * hv + h) * dv + col] = o * a.scale;
-        a.ring_d[(((size_t)slot * L + base + t) * hv + h) * dv + col] = d[t];
+        if (t % NQ == grp) {
+          a.out[((tok0 + t) * hv + h) * dv + col] = o * a.scale;
+          a.ring_d[(((size_t)slot * L + base + t) * hv + h) * dv + col] = d[t];
+        }
       }
     }
   }
 
-  // 10. wave 0: write_pos, and the window's keys and gates (shared by the key group / by
-  // the head's tiles)
+  // 10. wave 0: write_pos, and the window's keys and gates.  The keys are shared by the
+  // key group: one workgroup of it writes them.  GDN's gates are per head: each head's
+  // first column tile writes its own, except on a fold, where the rows written are rows
+  // other workgroups of the key group may still be reading, so the last of them writes all
+  // of the group's, one lane per (token, head).  (KDA: G = 1, the same workgroup.)
   if (wave == 0) {
     if (a.write_pos_out && h == 0 && vt == 0 && lane == 0) a.write_pos_out[row] = base;
     const bool writer = fold ? last : (h % a.G == 0 && vt == 0);
@@ -1000,18 +1010,18 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
           const int t = i / DK, r = i - t * DK;
           a.ring_g[(((size_t)slot * L + base + t) * hv + h) * DK + r] = to_f32(xg[t * KS + r]);
         }
-      } else if (lane == 0) {
-        for (int t = 0; t < T; ++t)
-          for (int g = 0; g < a.G; ++g) {
-            const int hh = kh * a.G + g;
-            a.ring_g[((size_t)slot * L + base + t) * hv + hh] =
-                load_bf16_uniform(gg + (tok0 + t) * hv + hh);
-          }
+      } else if (fold) {
+        for (int i = lane; i < T * a.G; i += 64) {
+          const int t = i / a.G, hh = kh * a.G + (i - t * a.G);
+          a.ring_g[((size_t)slot * L + t) * hv + hh] = to_f32(gg[(tok0 + t) * hv + hh]);
+        }
       }
       if (fold && lane == 0)
         __hip_atomic_store(a.group_counter + (size_t)row * hk + kh, 0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (!KDA && !fold && vt == 0 && lane < T)                     // (gate_s: this head's)
+      a.ring_g[((size_t)slot * L + base + lane) * hv + h] = pick(gate_s, lane);
   }
 }
 
