@@ -318,7 +318,8 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
     } else {
       for (int i = 0; i < nh; ++i) Gam *= hg[i];
     }
-    if (tid < DK) {
+    // (the MFMA readouts of the split fp32 state and of a bf16 state take q, k raw)
+    if (!F32_SPLIT && !BF16_MFMA && tid < DK) {
       float xq[TMAX], xk[TMAX];
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {                   // rows < 2*TMAX: in bounds
@@ -326,16 +327,14 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         xk[t] = to_f32(xkq[(T + t) * KS + tid]);
       }
       const float scale = fold ? 1.f : Gam;
-      if constexpr (!(F32_SPLIT && TMAX == 8)) {         // (no fp32 readout vectors there)
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-          if (t < T) {
-            xr[(2 * t) * XS + tid] = (scale * Gp[t]) * xq[t];
-            xr[(2 * t + 1) * XS + tid] = (scale * Gp[t]) * xk[t];
-          }
+      for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+          xr[(2 * t) * XS + tid] = (scale * Gp[t]) * xq[t];
+          xr[(2 * t + 1) * XS + tid] = (scale * Gp[t]) * xk[t];
         }
-        for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
       }
+      for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
     } else if (wave == 2 && L > 16) {
       // gamma_i = prod_{i<j<nh} alpha_j: an inclusive suffix product over the lanes of
       // one wave, shifted by one lane (rings up to 64 records; longer rings loop)
@@ -368,6 +367,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         xs[(T + t) * XS + tid] = k;
       }
       float g = 1.f;
+#pragma unroll 4
       for (int i = nh - 1; i >= 0; --i) {            // khat replaces the gates in place
         const float al = hg[i * DK + tid];
         khat[i * DK + tid] = g * to_f32(hkeys[i * KS + tid]);
@@ -514,19 +514,27 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       const float Gm = KDA ? 1.f : gate_product(gate_s, -1, tv);
       for (int cb = wave; cb < NCB; cb += kWaves) {
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < (hrows + 3) >> 2; ++ks) {
-          const int rec = 4 * ks + g4;
-          const bool ok = rec < hrows;
-          const int rs = ok ? rec : 0;                     // a row that exists; selected away
-          const float dv_ = hd[rs * BV + cb * 16 + l16];
-          float w;
-          if (KDA) {
-            const int plane = lay.lp * CS, o = rs * CS + (mok ? colm : 0);
-            w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
-          } else {
-            w = (Cs[rs * CS + (mok ? colm : 0)] * gam_i[rs]) * Gm;
+        // four steps of four records at a time: their LDS reads go out together
+        for (int ks0 = 0; 4 * ks0 < hrows; ks0 += 4) {
+          float av[4], bv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int rec = 4 * (ks0 + u) + g4;
+            const bool ok = rec < hrows;
+            const int rs = ok ? rec : 0;                   // a row that exists; selected away
+            const float dv_ = hd[rs * BV + cb * 16 + l16];
+            float w;
+            if (KDA) {
+              const int plane = lay.lp * CS, o = rs * CS + (mok ? colm : 0);
+              w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
+            } else {
+              w = (Cs[rs * CS + (mok ? colm : 0)] * gam_i[rs]) * Gm;
+            }
+            av[u] = ok ? dv_ : 0.f;
+            bv[u] = (ok && mok) ? w : 0.f;
           }
-          acc = mfma_16x16x4(ok ? dv_ : 0.f, (ok && mok) ? w : 0.f, acc);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc = mfma_16x16x4(av[u], bv[u], acc);
         }
         // lane holds columns cb*16 + 4*g4 + j of vector vb*16 + l16
         if (mv < NP) store4(hist + mv * BV + cb * 16 + 4 * g4, acc);
