@@ -43,7 +43,12 @@ template <> struct Chunk<bf16> {
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+// x * sigmoid(x) = x / (1 + e^-x) on the hardware exp2 and reciprocal (each within about
+// an ulp): e^-x = 2^(-x log2 e); x -> -inf gives x * 0 = -0, x -> +inf gives x.
+__device__ __forceinline__ float silu(float x) {
+  const float e = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 // N fp32 values to 16 or 32 bytes of the output dtype (bf16: round to nearest even).
 template <int N>
