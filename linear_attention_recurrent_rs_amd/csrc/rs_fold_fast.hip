@@ -28,16 +28,16 @@ __global__ __launch_bounds__(kThreads) void fold_fast_kernel(FoldArgs a, FoldFas
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, q4 = lane >> 4;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
   const int L = a.L, dv = a.dv, hv = a.hv, hk = a.hk;
   int n = a.nrec[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   if (!MATERIALIZE && n == 0) return;                   // nothing to commit
-  const int kh = h / a.G, col0 = vt * BV;
+  const int kh = udiv(h, a.G), col0 = vt * BV;
 
   bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
   float* hd = reinterpret_cast<float*>(smem + lay.hd);
@@ -167,16 +167,16 @@ __global__ __launch_bounds__(kThreads, 4) void fold_bf16_kernel(FoldArgs a, Fold
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, lg = lane >> 4;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
   const int L = a.L, dv = a.dv, hv = a.hv, hk = a.hk;
   int n = a.nrec[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   if (!MATERIALIZE && n == 0) return;                   // nothing to commit
-  const int kh = h / a.G, col0 = vt * BV;
+  const int kh = udiv(h, a.G), col0 = vt * BV;
 
   bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
   float* hd = reinterpret_cast<float*>(smem + lay.hd);

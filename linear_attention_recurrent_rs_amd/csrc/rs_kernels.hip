@@ -189,14 +189,14 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a, RowWindo
   constexpr int VPP = (2 * TMAX < 8) ? 2 * TMAX : 8;
   const int tid = threadIdx.x;
   const int lid = xcd_remap(blockIdx.x, a.nblocks);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
 
   const int L = a.L, dk = a.dk, dv = a.dv, hv = a.hv, hk = a.hk;
-  const int kh = h / a.G, col0 = vt * BV;
+  const int kh = udiv(h, a.G), col0 = vt * BV;
   int T;
   size_t tok0;
   row_window(rw.cu_seqlens, rw.ntok, a.T, row, &T, &tok0);
@@ -383,16 +383,16 @@ template <bool KDA, typename AT, typename ST, int BV, bool MATERIALIZE>
 __global__ __launch_bounds__(kThreads) void fold_kernel(FoldArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lid = xcd_remap(blockIdx.x, a.nblocks);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;
   const int L = a.L, dk = a.dk, dv = a.dv, hv = a.hv;
   int n = a.nrec[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   if (!MATERIALIZE && n == 0) return;
-  const int kh = h / a.G, col0 = vt * BV;
+  const int kh = udiv(h, a.G), col0 = vt * BV;
 
   ST* tile_raw = reinterpret_cast<ST*>(smem + a.lay.tile_raw);
   float* khat = reinterpret_cast<float*>(smem + a.lay.khat);

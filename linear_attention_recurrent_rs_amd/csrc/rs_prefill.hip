@@ -72,9 +72,9 @@ __global__ __launch_bounds__(kThreads, 4) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lc = lane & 15, lg = lane >> 4;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
   int P;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 4) void prefill_kernel(PrefillArgs a) {
     if (h == 0 && vt == 0 && tid == 0) a.cursor[slot] = 0;
     return;
   }
-  const int hv = a.hv, hk = a.hk, dv = a.dv, kh = h / a.G, col0 = vt * kBV;
+  const int hv = a.hv, hk = a.hk, dv = a.dv, kh = udiv(h, a.G), col0 = vt * kBV;
   const bf16* qg = static_cast<const bf16*>(a.q);
   const bf16* kg = static_cast<const bf16*>(a.k);
   const bf16* vg = static_cast<const bf16*>(a.v);

@@ -20,13 +20,13 @@ __global__ __launch_bounds__(kThreads) void snapshot_verify_kernel(SnapArgs a) {
   constexpr int NG = kThreads / BV;
   const int tid = threadIdx.x, c = tid % BV, g = tid / BV;
   const int lid = xcd_remap(blockIdx.x, a.nblocks);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
   const int dk = a.dk, dv = a.dv, hv = a.hv, hk = a.hk, T = a.T;
-  const int kh = h / a.G, col0 = vt * BV, rp = dk / NG, r0 = g * rp;
+  const int kh = udiv(h, a.G), col0 = vt * BV, rp = dk / NG, r0 = g * rp;
 
   float* tile = sm;                  // [dk x BV]
   float* part = tile + dk * BV;      // [NG x BV]

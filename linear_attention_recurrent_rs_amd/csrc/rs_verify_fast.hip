@@ -181,14 +181,14 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   const int cc = ADJ ? lane / RL : tid % CC;
   const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
-  const int vt = lid % a.NV;
-  const int h = (lid / a.NV) % a.hv;
-  const int row = lid / (a.NV * a.hv);
+  const int vt = umod(lid, a.NV);
+  const int h = umod(udiv(lid, a.NV), a.hv);
+  const int row = udiv(lid, a.NV * a.hv);
   const int slot = a.slot_idx[row];
   if (slot < 0 || slot >= a.num_slots) return;          // null row: no reads, no writes
 
   const int L = a.L, hv = a.hv, hk = a.hk, dv = a.dv;
-  const int kh = h / a.G, col0 = vt * BV;
+  const int kh = udiv(h, a.G), col0 = vt * BV;
   int T;
   size_t tok0;
   // uniform decode (TMAX = 1) has T = 1 at compile time; every other window is read at run
