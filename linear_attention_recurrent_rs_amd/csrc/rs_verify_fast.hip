@@ -315,6 +315,25 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       Gam = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
       const float ex = dpp_one<0x101>(v);
       if (wave == 2 && lane < nh) gam_i[lane] = ex;
+    } else if (L <= 64) {
+      // Rings up to 64 records: the same scan in each 16-lane row, then the rows joined
+      // through their totals (lanes 0, 16, 32, 48): the product over (i, nh) is row i/16's
+      // partial from lane i + 1 times the totals of the rows after it.
+      const int rw = lane >> 4;
+      float v = lane < nh ? hg[lane] : 1.f;
+      v *= dpp_one<0x101>(v);
+      v *= dpp_one<0x102>(v);
+      v *= dpp_one<0x104>(v);
+      v *= dpp_one<0x108>(v);
+      const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+      const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+      const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+      const float t3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+      const float f2 = t3, f1 = t2 * t3, f0 = t1 * f1;
+      Gam = t0 * f0;
+      const float F = rw == 0 ? f0 : rw == 1 ? f1 : rw == 2 ? f2 : 1.f;
+      const float ex = dpp_one<0x101>(v) * F;
+      if (wave == 2 && lane < nh) gam_i[lane] = ex;
     } else {
       for (int i = 0; i < nh; ++i) Gam *= hg[i];
     }
@@ -335,25 +354,13 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         }
       }
       for (int m = nvec; m < lay.nvec_pad; ++m) xr[m * XS + tid] = 0.f;
-    } else if (wave == 2 && L > 16) {
-      // gamma_i = prod_{i<j<nh} alpha_j: an inclusive suffix product over the lanes of
-      // one wave, shifted by one lane (rings up to 64 records; longer rings loop)
-      if (L <= 64) {
-        float v = lane < nh ? hg[lane] : 1.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float o = __shfl_down(v, off);
-          if (lane + off < 64) v *= o;
-        }
-        float ex = __shfl_down(v, 1);
-        if (lane == 63) ex = 1.f;
-        if (lane < nh) gam_i[lane] = ex;
-      } else {
-        for (int i = lane; i < nh; i += 64) {
-          float g = 1.f;
-          for (int j = i + 1; j < nh; ++j) g *= hg[j];
-          gam_i[i] = g;
-        }
+    } else if (wave == 2 && L > 64) {
+      // gamma_i = prod_{i<j<nh} alpha_j for rings past 64 records (rings up to 64 have
+      // theirs from the scan above)
+      for (int i = lane; i < nh; i += 64) {
+        float g = 1.f;
+        for (int j = i + 1; j < nh; ++j) g *= hg[j];
+        gam_i[i] = g;
       }
     }
   } else {
@@ -484,11 +491,11 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         sq += (a4[0] + a4[1]) + (a4[2] + a4[3]);
         sk += (b4[0] + b4[1]) + (b4[2] + b4[3]);
       }
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        sq += __shfl_xor(sq, off);
-        sk += __shfl_xor(sk, off);
-      }
+      // sums over the 16 lanes of the pair by DPP (quads, half rows, then the row mirror)
+      sq = adjacent_sum<8>(sq);
+      sk = adjacent_sum<8>(sk);
+      sq += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sq), 0x140, 0xF, 0xF, false));
+      sk += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sk), 0x140, 0xF, 0xF, false));
       if (e == 0) {
         Qm[t * TMAX + u] = sq;
         if (u < t) Am[t * TMAX + u] = pick(beta_s, t) * sk;
