@@ -156,7 +156,7 @@ struct FastLayout {
   int Gam;      // KDA: total history decay per key channel, fp32 [128]
   int xs;       // KDA: window vectors times the in-window prefix decay [2*tmax x xs_stride]
   int xr;       // readout vectors, q_t and k_t interleaved [nvec_pad x xs_stride]
-  int C;        // history scores [lp x cs] (GDN: undecayed) or 4 partial sums of them (KDA)
+  int C;        // history scores [lp x cs] (GDN: undecayed; KDA: of the decayed keys)
   int red;      // per-wave readout partial sums [4 x vpp x bv]; all vectors on the MFMA
                 //   readout (bv 64, tmax >= 8): [4 x nvec_pad x bv]
   int hist;     // history part of the readout [nvec_pad x bv] (MFMA readout only)
@@ -221,7 +221,7 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
     l.xs = o; o += al(2 * tmax * l.xs_stride * 4);
     const int dead_end = o;
     l.xr = o; o += al(l.nvec_pad * l.xs_stride * 4);
-    l.C = o; o += al(4 * l.lp * l.cs * 4);
+    l.C = o; o += al(l.lp * l.cs * 4);
     if (dead_end - dead >= red_bytes) {
       l.red = dead;
     } else {

@@ -221,8 +221,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   const bf16* gg = static_cast<const bf16*>(a.gate);
   const bf16* rkg = static_cast<const bf16*>(a.ring_k);
 
-  // 1. scalars through the scalar cache, before anything writes memory: the cursor, and
-  // the window's betas and (GDN) gates
+  // 1. the cursor through the scalar cache, before anything writes memory
   int n = a.cursor[slot];
   n = n < 0 ? 0 : (n > L ? L : n);
   const bool fold = n + T > L;                           // the window would overflow
@@ -232,13 +231,6 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
     if (a.write_pos_out && h == 0 && vt == 0 && tid == 0) a.write_pos_out[row] = base;
     return;
   }
-  float beta_s[TMAX], gate_s[TMAX], Gp[TMAX];
-#pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    beta_s[t] = t < T ? load_bf16_uniform(bg + (tok0 + t) * hv + h) : 0.f;
-    gate_s[t] = (!KDA && t < T) ? load_bf16_uniform(gg + (tok0 + t) * hv + h) : 0.f;
-  }
-
   // 2. window operands and the committed history [0, n): HBM -> LDS, asynchronous
   dma_rows_256(qg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, T, xkq, KS * 2);
   dma_rows_256(kg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, T, xkq + T * KS, KS * 2);
@@ -277,6 +269,15 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
     }
   }
   code_fence();
+  // the window's betas and (GDN) gates through the scalar cache, issued behind the loads:
+  // the history copies wait only for the cursor (a wait for one scalar load is a wait for
+  // all of them), and these land while the copies do
+  float beta_s[TMAX], gate_s[TMAX], Gp[TMAX];
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t) {
+    beta_s[t] = t < T ? load_bf16_uniform(bg + (tok0 + t) * hv + h) : 0.f;
+    gate_s[t] = (!KDA && t < T) ? load_bf16_uniform(gg + (tok0 + t) * hv + h) : 0.f;
+  }
   lds_barrier<NTILE>();                                  // every copy but the tile is in LDS
   // fp32 state, on a fold: the arrival of this workgroup at its key group's counter (step 7
   // explains it), now that its reads of the ring are complete, so that the round trip of
@@ -453,26 +454,31 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
   } else {
-    // history scores: fp32 MFMAs, wave w sums dk entries [32w, 32w + 32)
+    // history scores: fp32 MFMAs over the whole of dk, one 16 x 16 tile per wave, from
+    // wave 3 down (waves 0 and 1 take the window pairs below), so the scores land in LDS
+    // complete and their readers read one value per score
     const int RT = (hrows + 15) >> 4, CT = (nvec + 15) >> 4;
-    for (int tile = 0; tile < RT * CT; ++tile) {
+    for (int tile = kWaves - 1 - wave; tile < RT * CT; tile += kWaves) {
       const int rt = CT == 1 ? tile : tile >> 1, ct = CT == 1 ? 0 : tile & 1;
       const int ra = rt * 16 + l16, m = ct * 16 + l16;
       const bool aok = ra < hrows, bok = m < nvec;
       const float* ap = khat + (aok ? ra : 0) * DK;
       const float* bp = xs + (bok ? m : 0) * XS;
-      float av[8], bv[8];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        av[st] = ap[32 * wave + 4 * st + g4];
-        bv[st] = bp[32 * wave + 4 * st + g4];
-      }
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) acc = mfma_16x16x4(aok ? av[st] : 0.f, bok ? bv[st] : 0.f, acc);
-      float* part = Cs + wave * lay.lp * CS;
+      for (int q = 0; q < DK / 32; ++q) {                  // eight K steps at a time
+        float av[8], bv[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[(rt * 16 + 4 * g4 + j) * CS + m] = acc[j];
+        for (int st = 0; st < 8; ++st) {
+          av[st] = ap[32 * q + 4 * st + g4];
+          bv[st] = bp[32 * q + 4 * st + g4];
+        }
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          acc = mfma_16x16x4(aok ? av[st] : 0.f, bok ? bv[st] : 0.f, acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Cs[(rt * 16 + 4 * g4 + j) * CS + m] = acc[j];
     }
     // window pairs: per-channel decays between u and t, 16 lanes per pair
     const int npair = T * (T + 1) / 2, grp = tid >> 4, e = tid & 15;
@@ -506,7 +512,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
 
   // 6. (many window vectors) history part of the readout, before the tile is touched:
   //   hist[m][c] = sum_i d_i[c] w_i[m],  w_i[m] = gamma_i G_t(m) (k_i . x_m)  (GDN; KDA: the
-  //   summed partial scores), vectors m in readout order.  An MFMA contraction over the
+  //   decayed keys' scores khat_i . x_m), vectors m in readout order.  An MFMA contraction over the
   //   records: A = d_i of 16 columns, B = w_i of 16 vectors, four records per step; wave w
   //   takes the column blocks w, w + 4, ...  (With few vectors the readout itself adds
   //   the history part, step 8.)
@@ -532,8 +538,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
             const float dv_ = hd[rs * BV + cb * 16 + l16];
             float w;
             if (KDA) {
-              const int plane = lay.lp * CS, o = rs * CS + (mok ? colm : 0);
-              w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
+              w = Cs[rs * CS + (mok ? colm : 0)];
             } else {
               w = (Cs[rs * CS + (mok ? colm : 0)] * gam_i[rs]) * Gm;
             }
@@ -908,7 +913,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       for (int mm = 0; mm < VPP; ++mm) acc[mm] = f4{0.f, 0.f, 0.f, 0.f};
       // history part first (it needs no tile): row group rg takes records rg, rg + RG, ...
       // and adds d_i[4 columns] * w_i[m], w_i[m] = gamma_i G_t(m) (k_i . x_m) (KDA: the
-      // summed partial scores); the lane sums below reduce it with the tile part
+      // decayed keys' scores); the lane sums below reduce it with the tile part
       for (int i = rg; i < hrows; i += RG) {
         const f4 dq = load4(hd + i * BV + 4 * cc);
         const float gi = KDA ? 1.f : gam_i[i];
@@ -918,8 +923,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
           if (mv < nvec) {
             float w;
             if (KDA) {
-              const int plane = lay.lp * CS, o = i * CS + col;
-              w = (Cs[o] + Cs[plane + o]) + (Cs[2 * plane + o] + Cs[3 * plane + o]);
+              w = Cs[i * CS + col];
             } else {
               w = (Cs[i * CS + col] * gi) * Gp[t];
             }
