@@ -33,13 +33,55 @@
 
 namespace rs {
 
+// The aligned 32-bit word holding the bf16 at p, through the scalar cache (p uniform);
+// hi: whether the value is the word's high half.
+__device__ __forceinline__ uint32_t load_word_uniform(const bf16* p, int& hi) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  hi = (a & 2) != 0;
+  return *(const __attribute__((address_space(4))) uint32_t*)(a & ~uintptr_t(3));
+}
+
 // A bf16 value at a workgroup-uniform address, through the scalar data cache.
 __device__ __forceinline__ float load_bf16_uniform(const bf16* p) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const __attribute__((address_space(4))) uint32_t* w =
-      (const __attribute__((address_space(4))) uint32_t*)(a & ~uintptr_t(3));
-  const uint32_t v = *w;
-  return __uint_as_float((a & 2) ? (v & 0xffff0000u) : (v << 16));
+  int hi;
+  const uint32_t w = load_word_uniform(p, hi);
+  return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+}
+
+// The bf16 in the high (odd element) or low half of a word, as fp32.
+__device__ __forceinline__ float bf16_half(uint32_t w, int hi) {
+  return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16));
+}
+
+// N uniform words, all loaded by this point (an empty asm reads up to eight together).
+template <int N>
+__device__ __forceinline__ void pin_words(uint32_t* w) {
+  if constexpr (N == 1) asm volatile("" : "+s"(w[0]));
+  else if constexpr (N == 2) asm volatile("" : "+s"(w[0]), "+s"(w[1]));
+  else if constexpr (N == 3) asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]));
+  else if constexpr (N == 4) asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]));
+  else if constexpr (N == 5)
+    asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(w[4]));
+  else if constexpr (N == 6)
+    asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(w[4]), "+s"(w[5]));
+  else if constexpr (N == 7)
+    asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(w[4]), "+s"(w[5]),
+                 "+s"(w[6]));
+  else if constexpr (N == 8)
+    asm volatile("" : "+s"(w[0]), "+s"(w[1]), "+s"(w[2]), "+s"(w[3]), "+s"(w[4]), "+s"(w[5]),
+                 "+s"(w[6]), "+s"(w[7]));
+  else {                                                 // eight at a time
+    pin_words<8>(w);
+    pin_words<N - 8>(w + 8);
+  }
+}
+
+// A workgroup-uniform value, computed by this point and held in a scalar register from here
+// on (the empty asm takes it there and keeps the compiler from sinking its computation).
+__device__ __forceinline__ float pin_uniform(float x) {
+  uint32_t u = __builtin_amdgcn_readfirstlane(__float_as_uint(x));
+  asm volatile("" : "+s"(u));
+  return __uint_as_float(u);
 }
 
 __device__ __forceinline__ f4 bf16x4(const bf16* p) { return load4(p); }
@@ -284,10 +326,38 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   // the history copies wait only for the cursor (a wait for one scalar load is a wait for
   // all of them), and these land while the copies do
   float beta_s[TMAX], gate_s[TMAX], Gp[TMAX];
+  if constexpr (TMAX <= 3) {
+    // a short window: the loads under their branches, a round trip each, hide behind the
+    // tile (window 3 decodes measured 32.7 us so against 33.4 us batched)
 #pragma unroll
-  for (int t = 0; t < TMAX; ++t) {
-    beta_s[t] = t < T ? load_bf16_uniform(bg + (tok0 + t) * hv + h) : 0.f;
-    gate_s[t] = (!KDA && t < T) ? load_bf16_uniform(gg + (tok0 + t) * hv + h) : 0.f;
+    for (int t = 0; t < TMAX; ++t) {
+      beta_s[t] = t < T ? load_bf16_uniform(bg + (tok0 + t) * hv + h) : 0.f;
+      gate_s[t] = (!KDA && t < T) ? load_bf16_uniform(gg + (tok0 + t) * hv + h) : 0.f;
+    }
+  } else {
+    // a long one: every word is loaded (a short ragged window repeats its last token,
+    // 1 <= T here) and the empty asm needs them all at once, so one wait covers them (the
+    // large-ring verify at window 8 measured 233 against 293 us with a wait per load)
+    constexpr int NW = KDA ? TMAX : 2 * TMAX;            // words: betas, then (GDN) gates
+    uint32_t wd[NW];
+    int hi[NW];                                          // the value is the word's high half
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int e = (tok0 + (t < T ? t : T - 1)) * hv + h;
+      wd[t] = load_word_uniform(bg + e, hi[t]);
+      if constexpr (!KDA) wd[TMAX + t] = load_word_uniform(gg + e, hi[TMAX + t]);
+    }
+    pin_words<NW>(wd);
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      // the values, not the words and their halves, live on from here: left to itself
+      // the compiler keeps the words, and spills
+      beta_s[t] = t < T ? pin_uniform(bf16_half(wd[t], hi[t])) : 0.f;
+      if constexpr (!KDA)
+        gate_s[t] = t < T ? pin_uniform(bf16_half(wd[TMAX + t], hi[TMAX + t])) : 0.f;
+      else
+        gate_s[t] = 0.f;
+    }
   }
   lds_barrier<NTILE>();                                  // every copy but the tile is in LDS
   // fp32 state, on a fold: the arrival of this workgroup at its key group's counter (step 7
