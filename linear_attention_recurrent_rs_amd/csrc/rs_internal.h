@@ -166,6 +166,12 @@ struct FastLayout {
   int nvec_pad;
   int cs;       // row stride of C: 2*tmax rounded up to 16
   int lp;       // rows of C: L rounded up to 16
+  int kreg;     // 1: GDN fp32 state, 64-column tiles, windows 5..8, ring of 17..64 records:
+                //   the history keys go to registers (each wave the keys of its 16-row
+                //   score tile), not to hkeys; a folding workgroup, which forms no history
+                //   scores, copies them unpadded to fkeys instead
+  int fkeys;    // (kreg) a folding workgroup's history keys, bf16 [L x 128], over C, hist
+                //   and the space after them
 };
 
 constexpr int kKeyStride = 136;   // 128 bf16 + 16 bytes of padding
@@ -228,15 +234,16 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
       l.red = o; o += red_bytes;
     }
   } else {
+    const bool split8 = fast_f32_split(kda, bf16_state, bv, tmax) && tmax == 8;
+    l.kreg = split8 && L > 16 && L <= 64;
     l.xg = o;
-    l.hkeys = o; o += al(L * ks * 2);
+    l.hkeys = o; o += l.kreg ? 0 : al(L * ks * 2);
     l.hd = o; o += al(L * bv * 4);
     l.hg = o; o += al(L * 4);
     l.gam_i = o; o += al(L * 4);
     l.khat = o;
     l.Gam = o;
     l.xs = o;
-    const bool split8 = fast_f32_split(kda, bf16_state, bv, tmax) && tmax == 8;
     l.xr = o; o += split8 ? 0 : al(l.nvec_pad * l.xs_stride * 4);
     l.C = o; o += al(l.lp * l.cs * 4);
     // per-wave partials: of one pass of vpp vectors, or of all vectors (MFMA readouts).  The
@@ -250,6 +257,10 @@ inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T
     }
   }
   l.hist = o; o += all_vec ? al(l.nvec_pad * bv * 4) : 0;
+  if (l.kreg) {                                          // C and hist are adjacent
+    l.fkeys = l.C;
+    if (o < l.C + al(L * 128 * 2)) o = l.C + al(L * 128 * 2);
+  }
   l.Am = o; o += al(tmax * tmax * 4);
   l.Qm = o; o += al(tmax * tmax * 4);
   l.total = o;

@@ -205,6 +205,9 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   // KDA with an fp32 state, 64-column tiles, window 4: readout on bf16 MFMAs with both
   // operands split (step 8)
   constexpr bool KDA_SPLIT = fast_kda_split(KDA, sizeof(ST) == 2, BV, TMAX);
+  // history keys in registers (when the plan says so, lay.kreg: rings of 17..64 records),
+  // so that the LDS plan leaves room for a fourth workgroup per CU
+  constexpr bool KREG = F32_SPLIT && TMAX == 8;
   constexpr int NTILE = BF16_MFMA ? 8 : QPT * 4;          // tile load instructions
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Lane mapping.  Column quad fastest (cc = lane % CC) makes 16 consecutive lanes read
@@ -243,6 +246,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   bf16* xv = reinterpret_cast<bf16*>(smem + lay.xv);
   bf16* xg = reinterpret_cast<bf16*>(smem + lay.xg);
   bf16* hkeys = reinterpret_cast<bf16*>(smem + lay.hkeys);
+  bf16* fkeys = reinterpret_cast<bf16*>(smem + lay.fkeys);
   float* hd = reinterpret_cast<float*>(smem + lay.hd);
   float* hg = reinterpret_cast<float*>(smem + lay.hg);
   float* gam_i = reinterpret_cast<float*>(smem + lay.gam_i);
@@ -289,9 +293,14 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
     dma_rows_256(kg + (tok0 * hk + kh) * DK, (size_t)hk * DK * 2, T, xkq + T * KS, KS * 2);
     dma_rows(vg + (tok0 * hv + h) * dv + col0, (size_t)hv * dv * 2, BV * 2, T, xv);
   }
+  const bool kreg = KREG && lay.kreg;
   if (nh > 0) {
-    dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, nh, hkeys,
-                 KS * 2);
+    if (!kreg)
+      dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, nh, hkeys,
+                   KS * 2);
+    else if (fold)                                       // for the fold only, unpadded
+      dma_rows_256(rkg + ((size_t)slot * L * hk + kh) * DK, (size_t)hk * DK * 2, nh, fkeys,
+                   DK * 2);
     dma_rows(a.ring_d + ((size_t)slot * L * hv + h) * dv + col0, (size_t)hv * dv * 4, BV * 4,
              nh, hd);
     if (KDA)
@@ -301,6 +310,20 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   }
   code_fence();
 
+  // (kreg, no fold) the history keys of this wave's score tile (step 5), HBM -> registers,
+  // behind the variable-length copies so that their wait counts only the tile: record
+  // 16 wave + lane % 16, dk 16 ks + 4 (lane / 16) .. +3 in kk[ks], the layout of the MFMA's
+  // A operand.  Lanes past the history load record 0 (selected away in step 5).
+  u2 kk[8];
+  if constexpr (KREG) {
+    if (kreg && !fold) {
+      const int rec = 16 * wave + (lane & 15);
+      const bf16* kp = rkg + (((size_t)slot * L + (rec < nh ? rec : 0)) * hk + kh) * DK +
+                       4 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kk[ks] = *reinterpret_cast<const u2*>(kp + 16 * ks);
+    }
+  }
   // 3. the state tile: HBM -> registers, the last vector loads issued before the wait
   const ST* sg = static_cast<const ST*>(a.state) + (((size_t)slot * hv + h) * DK) * dv + col0;
   f4 s[QPT][4];
@@ -496,7 +519,11 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       const int ra = rt * 16 + l16, m = ct * 16 + l16;
       const bool aok = ra < R, bok = m < nvec;
       // operands from rows that always exist; rows outside the tile are selected away
-      const bf16* ap = ra < hrows ? hkeys + ra * KS : xkq + (T + (aok ? ra - hrows : 0)) * KS;
+      // (kreg: a history row's keys are this lane's registers, tile == wave here, for the
+      // R <= L <= 64 rows of a window that does not fold make at most four row tiles)
+      const bool areg = kreg && ra < hrows;
+      const bf16* ap = (ra < hrows && !kreg) ? hkeys + ra * KS
+                                             : xkq + (T + (aok && !areg ? ra - hrows : 0)) * KS;
       const bf16* bp = xkq + (bok ? m : 0) * KS;
       const s4 zero = s4{0, 0, 0, 0};
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
@@ -507,6 +534,8 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         for (int kb = 0; kb < DK / 32; ++kb) {
           const int k0 = (half * (DK / 32) + kb) * 16 + 4 * g4;
           av[kb] = *reinterpret_cast<const s4*>(ap + k0);
+          if constexpr (KREG)
+            if (areg) av[kb] = __builtin_bit_cast(s4, kk[half * (DK / 32) + kb]);
           bv[kb] = *reinterpret_cast<const s4*>(bp + k0);
         }
 #pragma unroll
@@ -717,6 +746,8 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       // l / 16 taking records 4 (l / 16) .. +3 of the block; records past n are selected
       // to zero, never read into the product.
       const int lc = lane & 15, lg = lane >> 4;
+      const bf16* fk = kreg ? fkeys : hkeys;
+      const int fks = kreg ? DK : KS;
       for (int rb = 0; rb < nh; rb += 16) {
         int recs[4];
         bool ok[4];
@@ -732,7 +763,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
           const int row = 16 * wave + 64 * j + lc;
           s4 kv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kv[e] = ok[e] ? short(hkeys[recs[e] * KS + row]) : short(0);
+          for (int e = 0; e < 4; ++e) kv[e] = ok[e] ? short(fk[recs[e] * fks + row]) : short(0);
           ka[j] = kv;
         }
 #pragma unroll

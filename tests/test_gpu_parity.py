@@ -162,10 +162,12 @@ def test_key_group_xcd_order(name, cfg):
     _run(cfg)
 
 
-@pytest.mark.parametrize('T,L', [(4, 16), (6, 24), (16, 16)])
+@pytest.mark.parametrize('T,L', [(4, 16), (6, 24), (8, 40), (16, 16)])
 def test_wide_windows(T, L):
     """fp32 state, 64-column tiles, windows of 4 and more (from 5 on, the readout over the
-    tile runs as an MFMA contraction; T = 16: two blocks of 16 window vectors)."""
+    tile runs as an MFMA contraction; T = 16: two blocks of 16 window vectors).  Windows of
+    5..8 over rings of 17..64 records hold the history keys in registers, and a folding
+    workgroup copies them over the scores (rings of 24 and 40 records here)."""
     cfg = W.CONFIGS['c1'].with_(B=6, null_rows=1, hk=2, hv=4, T=T, L=L,
                                 accept=('uniform', 0, T), steps=8, cursor_init='zero')
     _run(cfg)
