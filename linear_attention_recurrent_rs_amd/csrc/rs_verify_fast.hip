@@ -905,7 +905,30 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       }
     }
     lds_barrier();
-    if (SPREAD || tid < BV) {
+    if constexpr (SPREAD && BV == 64) {
+      // every thread needs the sums of its column: wave w forms those of vectors
+      // 4 w .. 4 w + 3 (not all of them, as one thread per column would), then they pass
+      // through the first partial plane
+      const float scale = fold ? 1.f : Gam;
+      const int c = tid % BV;
+      float mine[NV2 / 4];
+#pragma unroll
+      for (int q = 0; q < NV2 / 4; ++q) {
+        const int m = 4 * wave + q;
+        float p = (red[m * BV + c] + red[(NPd + m) * BV + c]) +
+                  (red[(2 * NPd + m) * BV + c] + red[(3 * NPd + m) * BV + c]);
+        p *= scale * pick(Gp, m >> 1);
+        if (hrows > 0) p += hist[m * BV + c];
+        mine[q] = p;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int q = 0; q < NV2 / 4; ++q) red[(4 * wave + q) * BV + c] = mine[q];
+      lds_barrier();
+#pragma unroll
+      for (int m = 0; m < NV2; ++m)
+        if (m < nvec) Pv[m] = red[m * BV + c];
+    } else if (SPREAD || tid < BV) {
       const float scale = fold ? 1.f : Gam;
 #pragma unroll
       for (int m = 0; m < NV2; ++m) {
