@@ -190,11 +190,13 @@ __host__ __device__ constexpr bool fast_f32_split(bool kda, bool bf16_state, int
   return !kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4 || tmax == 8);
 }
 
-// The same for KDA (fp32 state, 64-column tiles, window 4): the decayed readout vectors
+// The same for KDA (fp32 state, 64-column tiles, windows 3..4): the decayed readout vectors
 // split into high and mid bf16 parts (kept where the fp32 vectors would be), the state into
-// high and low parts, three MFMAs per block.  (At window 3 the FMA readout measured faster.)
+// high and low parts, three MFMAs per block.  Its lane mapping also carries the fold on
+// fp32 MFMAs.  (At window 3 the FMA readout alone measured faster; with the MFMA fold the
+// pair measured 41.5 against 42.0 us.)
 __host__ __device__ constexpr bool fast_kda_split(bool kda, bool bf16_state, int bv, int tmax) {
-  return kda && !bf16_state && bv == 64 && tmax == 4;
+  return kda && !bf16_state && bv == 64 && (tmax == 3 || tmax == 4);
 }
 
 inline FastLayout fast_layout(bool kda, bool bf16_state, int bv, int tmax, int T, int L) {

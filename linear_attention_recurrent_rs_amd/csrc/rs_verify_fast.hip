@@ -219,10 +219,10 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   constexpr int RL = 64 / CC;                            // row groups per wave
   constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && !KDA_SPLIT && TMAX >= 3;
-  // GDN, fp32 state, 64-column tiles in this lane mapping, windows of 2 and more: the
-  // fused fold on bf16 MFMAs (step 7).  (At window 1 it frees enough registers for six
-  // workgroups per CU, which measured slower than the VALU fold at five.)
-  constexpr bool MFMA_FOLD = !KDA && sizeof(ST) == 4 && CC == 16 && !ADJ && TMAX >= 2;
+  // fp32 state, 64-column tiles in this lane mapping, windows of 2 and more: the fused
+  // fold on MFMAs (step 7; GDN bf16, KDA fp32).  (At window 1 it frees enough registers
+  // for six workgroups per CU, which measured slower than the VALU fold at five.)
+  constexpr bool MFMA_FOLD = sizeof(ST) == 4 && CC == 16 && !ADJ && TMAX >= 2;
   const int cc = ADJ ? lane / RL : tid % CC;
   const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
@@ -737,7 +737,34 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[j][i] *= KDA ? Gamv[r0 + i] : Gam;
     }
-    if constexpr (MFMA_FOLD) {
+    if constexpr (MFMA_FOLD && KDA) {
+      // S += Khat D^T over records on v_mfma_f32_16x16x4_f32, the tile registers the
+      // accumulators (lane l: rows 16 wave + 64 j + 4 (l / 16) + i at column 4 (l % 16)
+      // + jj, element i of D[4 (l / 16) + i][l % 16]): A = the decayed keys khat_i (fp32),
+      // B = d_i, lane group l / 16 taking record rb + l / 16; records past n are selected
+      // to zero.
+      const int lc = lane & 15, lg = lane >> 4;
+      for (int rb = 0; rb < nh; rb += 4) {
+        const int rec = rb + lg;
+        const bool ok = rec < nh;
+        const int rs = ok ? rec : 0;
+        float ka[QPT];
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) ka[j] = ok ? khat[rs * DK + 16 * wave + 64 * j + lc] : 0.f;
+        const f4 dq = load4(hd + rs * BV + 4 * lc);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float b = ok ? dq[jj] : 0.f;
+#pragma unroll
+          for (int j = 0; j < QPT; ++j) {
+            f4 acc = f4{s[j][0][jj], s[j][1][jj], s[j][2][jj], s[j][3][jj]};
+            acc = mfma_16x16x4(ka[j], b, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[j][i][jj] = acc[i];
+          }
+        }
+      }
+    } else if constexpr (MFMA_FOLD) {
       // S += K (gamma (.) D)^T over records in blocks of 16 on v_mfma_f32_16x16x16_bf16.
       // The tile registers are the accumulators: for fixed (j, jj), lane l holds rows
       // 16 wave + 64 j + 4 (l / 16) + i at column 4 (l % 16) + jj, which is element i of
