@@ -219,10 +219,11 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   constexpr bool MFMA_READOUT = (CC == 16 && TMAX >= 8);
   constexpr int RL = 64 / CC;                            // row groups per wave
   constexpr bool ADJ = !MFMA_READOUT && !F32_SPLIT && !KDA_SPLIT && TMAX >= 3;
-  // fp32 state, 64-column tiles in this lane mapping, windows of 2 and more: the fused
-  // fold on MFMAs (step 7; GDN bf16, KDA fp32).  (At window 1 it frees enough registers
-  // for six workgroups per CU, which measured slower than the VALU fold at five.)
-  constexpr bool MFMA_FOLD = sizeof(ST) == 4 && CC == 16 && !ADJ && TMAX >= 2;
+  // fp32 state, 64-column tiles in this lane mapping: the fused fold on MFMAs (step 7; GDN
+  // bf16, KDA fp32; KDA from window 2).  At window 1 it frees enough registers for six
+  // workgroups per CU, which measured slower than five (28.3 against 27.7 us): the LDS
+  // plan holds that kernel at five (fast_layout).
+  constexpr bool MFMA_FOLD = sizeof(ST) == 4 && CC == 16 && !ADJ && (TMAX >= 2 || !KDA);
   const int cc = ADJ ? lane / RL : tid % CC;
   const int rg = ADJ ? wave * RL + lane % RL : tid / CC;
   const int lid = xcd_group_remap(blockIdx.x, a.nblocks, a.G * a.NV);
