@@ -547,6 +547,20 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
         const bool isq = m < T;
         const int t = isq ? m : m - T;
         const int r0 = rt * 16 + 4 * g4;
+        // (windows of 8 and more) the window decays G(u, t) of this lane's rows u = r0 + j -
+        // hrows, from the last row up, each from the one after it (rows of the history
+        // take unused values); shorter windows form each on its own, in fewer registers
+        float decs[4];
+        if (TMAX >= 8 && r0 + 3 >= hrows) {
+          float p = gate_product(gate_s, r0 + 3 - hrows, t);
+          decs[3] = p;
+#pragma unroll
+          for (int j = 2; j >= 0; --j) {
+            const int u = r0 + j - hrows;
+            if (u < t) p *= pick(gate_s, u + 1);
+            decs[j] = p;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rr = r0 + j;
@@ -554,7 +568,7 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
             Cs[rr * CS + m] = acc[j];
           } else if (rr < R) {
             const int u = rr - hrows;
-            const float dec = gate_product(gate_s, u, t);
+            const float dec = TMAX >= 8 ? decs[j] : gate_product(gate_s, u, t);
             if (isq) {
               if (u <= t) Qm[t * TMAX + u] = acc[j] * dec;
             } else if (u < t) {
@@ -635,7 +649,8 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       const int mv = vb * 16 + l16;                        // this lane's vector (B column)
       const bool mok = mv < nvec;
       const int tv = mv >> 1, colm = (mv & 1) ? T + tv : tv;
-      const float Gm = KDA ? 1.f : gate_product(gate_s, -1, tv);
+      // G_tv = prod_{w<=tv} alpha_w (windows of 8 and more: Gp[tv], by selection)
+      const float Gm = KDA ? 1.f : TMAX >= 8 ? pick(Gp, tv) : gate_product(gate_s, -1, tv);
       for (int cb = wave; cb < NCB; cb += kWaves) {
         f4 acc = f4{0.f, 0.f, 0.f, 0.f};
         // four steps of four records at a time: their LDS reads go out together
