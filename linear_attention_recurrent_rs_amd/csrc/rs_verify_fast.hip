@@ -158,12 +158,14 @@ __device__ __forceinline__ void store_tile(ST* so, const f4 (&s)[QPT][4], int rg
 
 // Workgroups per CU the register cap is set for.  More resident workgroups keep more tile
 // bytes in flight, so the cap is raised where that fits without spills and measures
-// faster: six per CU (at most 80 VGPRs) for 64-column tiles at windows 2-3 (KDA: 2), five
-// (96 VGPRs) for the other 64-column tiles up to window 3 and GDN's at window 4, four (128
-// VGPRs) for 128-column bf16 tiles up to window 3.  (At window 1 six per CU fit too but
-// run slower; KDA at window 4 would spill under five.)
+// faster: six per CU (at most 80 VGPRs) for 64-column tiles at windows 2-3 (KDA at window
+// 3: its split readout, whose LDS plan also fits six), five (96 VGPRs) for the other
+// 64-column tiles up to window 3 and GDN's at window 4, four (128 VGPRs) for 128-column
+// bf16 tiles up to window 3.  (At window 1 six per CU fit too but run slower; KDA at
+// window 4 would spill under five.)
 constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
   return (bv <= 64 && (tmax == 2 || (tmax == 3 && !kda))) ? 6
+         : fast_kda_split(kda, bf16_state, bv, tmax) && tmax == 3 ? 6
          : (bv <= 64 && (tmax <= 3 || (tmax == 4 && !kda))) ? 5
          : fast_bf16_mfma(kda, bf16_state, bv, tmax)       ? 5
          : (bv == 128 && bf16_state && tmax <= 3)          ? 4
@@ -630,6 +632,16 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
       if (e == 0) {
         Qm[t * TMAX + u] = sq;
         if (u < t) Am[t * TMAX + u] = pick(beta_s, t) * sk;
+      }
+    }
+    // the window's gates to the ring, on a window that does not fold (rows past the
+    // history, which no workgroup reads this launch), by wave 2 while they are in LDS:
+    // the split readout's plan reuses their space from the next step on.  (On a fold the
+    // key group's last arriver writes them from the inputs, step 10.)
+    if (!fold && h % a.G == 0 && vt == 0 && wave == 2) {
+      for (int i = lane; i < T * DK; i += 64) {
+        const int t = i / DK, r = i - t * DK;
+        a.ring_g[(((size_t)slot * L + base + t) * hv + h) * DK + r] = to_f32(xg[t * KS + r]);
       }
     }
   }
@@ -1203,9 +1215,12 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
             *reinterpret_cast<const uint4*>(xkq + (T + t) * KS + c8);
       }
       if (KDA) {
-        for (int i = lane; i < T * DK; i += 64) {
-          const int t = i / DK, r = i - t * DK;
-          a.ring_g[(((size_t)slot * L + base + t) * hv + h) * DK + r] = to_f32(xg[t * KS + r]);
+        if (fold) {                                      // (not folding: step 5)
+          for (int i = lane; i < T * DK; i += 64) {
+            const int t = i / DK, r = i - t * DK;
+            a.ring_g[(((size_t)slot * L + t) * hv + h) * DK + r] =
+                to_f32(gg[((tok0 + t) * hv + h) * DK + r]);
+          }
         }
       } else if (fold) {
         for (int i = lane; i < T * a.G; i += 64) {
