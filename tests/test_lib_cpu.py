@@ -93,6 +93,21 @@ def test_launch_info():
     assert tv == 128 and wg == 64 * 32
 
 
+@pytest.mark.parametrize('kw,kda,per_cu', [
+    (dict(T=1), False, 5),                                  # the decode, held at five
+    (dict(T=3), False, 7),                                  # (its register cap sets six)
+    (dict(T=3, hk=32), True, 6),                            # KDA's compact split-readout plan
+    (dict(T=8, ring_cap=64, batch=256, num_slots=256), False, 4),   # history keys in registers
+])
+def test_launch_plan_residency(kw, kda, per_cu):
+    """Workgroups per CU that the verify's LDS plan allows (160 KiB of LDS a CU) for the
+    benchmark's shapes: the plans are laid out for these residencies."""
+    d = dict(batch=64, hk=16, hv=32, num_slots=96)
+    d.update(kw)
+    _, _, lds = rs.verify_launch_info(_dims(**d), kda=kda)
+    assert (160 * 1024) // lds == per_cu, lds
+
+
 def test_advance_and_fold_validation():
     lib = rs._lib()
     d = _dims()
