@@ -173,6 +173,18 @@ def test_wide_windows(T, L):
     _run(cfg)
 
 
+@pytest.mark.parametrize('T,L', [(3, 24), (3, 40), (4, 20)])
+def test_kda_rings(T, L):
+    """KDA, fp32 state, windows 3 and 4 (the split MFMA readout and the fp32-MFMA fold)
+    over rings that are not multiples of 16 records: at window 3 the LDS plan places the
+    history scores and the history readout over the window gates, raw keys and decayed
+    vectors, and the window's gates reach the ring during the scores (or, on a fold, from
+    the inputs)."""
+    cfg = W.CONFIGS['c3'].with_(B=5, hk=3, hv=3, T=T, L=L, accept=('uniform', 0, T),
+                                cursor_init='stagger', steps=24)
+    _run(cfg)
+
+
 @pytest.mark.parametrize('T', [2, 3, 4, 8])
 def test_bf16_state_history_and_fused_folds(T):
     """bf16 state, 128-column tiles (the readout on bf16 MFMAs), no commit folds: rows
