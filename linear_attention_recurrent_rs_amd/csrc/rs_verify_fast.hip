@@ -162,7 +162,7 @@ __device__ __forceinline__ void store_tile(ST* so, const f4 (&s)[QPT][4], int rg
 // 3: its split readout, whose LDS plan also fits six), five (96 VGPRs) for the other
 // 64-column tiles up to window 3 and GDN's at window 4, four (128 VGPRs) for 128-column
 // bf16 tiles up to window 3.  (At window 1 six per CU fit too but run slower; KDA at
-// window 4 would spill under five.)
+// window 4 fits five in 81 VGPRs, which measured the same as its four.)
 constexpr int fast_min_blocks(bool kda, int bv, int tmax, bool bf16_state) {
   return (bv <= 64 && (tmax == 2 || (tmax == 3 && !kda))) ? 6
          : fast_kda_split(kda, bf16_state, bv, tmax) && tmax == 3 ? 6
@@ -1203,7 +1203,8 @@ void verify_fast_kernel(VerifyArgs a, FastLayout lay, RowWindows rw) {
   // key group: one workgroup of it writes them.  GDN's gates are per head: each head's
   // first column tile writes its own, except on a fold, where the rows written are rows
   // other workgroups of the key group may still be reading, so the last of them writes all
-  // of the group's, one lane per (token, head).  (KDA: G = 1, the same workgroup.)
+  // of the group's, one lane per (token, head).  (KDA: G = 1, the same workgroup; its
+  // gates, rows of dk, were written during the scores unless the window folds.)
   if (wave == 0) {
     if (a.write_pos_out && h == 0 && vt == 0 && lane == 0) a.write_pos_out[row] = base;
     const bool writer = fold ? last : (h % a.G == 0 && vt == 0);
